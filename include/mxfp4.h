@@ -1,0 +1,167 @@
+/*
+ * mxfp4.h -- C ABI of the MI355X (gfx950) W4A4 MXFP4 linear-layer library.
+ *
+ * A W4A4 MXFP4 linear layer Y = X * W^T has two device steps:
+ *   1. mxfp4_quantize_rotate: online activation quantization.  Each row of X
+ *      is cut into 32-element blocks along K; each block is optionally
+ *      rotated (a normalized Hadamard-32 or a Kronecker-factored 32x32
+ *      transform), then shares one power-of-two E8M0 scale and is encoded as
+ *      4-bit E2M1 codes, two per byte.
+ *   2. mxfp4_gemm: a GEMM that reads the packed MXFP4 operands directly (no
+ *      dequantize pass), accumulates in fp32 and writes fp32 or bf16.
+ * Weights are quantized once, offline, with the same quantizer (the weight
+ * side of a rotation: the same Hadamard-32, or the inverse-transpose
+ * Kronecker factors from mxfp4_inverse_transpose).
+ *
+ * Sources (page titles and sections as the pages give them):
+ *  - "AMD Quark delivers MXFP4 quantization for FLUX.1-dev on Instinct MI350
+ *    with 1.92x speedup": "What is MXFP4 and why does it eliminate
+ *    dequantization overhead?" (32-element blocks sharing one scale, 4-bit
+ *    elements, the MX specification) and "MXFP4 quantization for diffusion
+ *    models" (the GEMM consumes MXFP4 directly, no dequantization phase).
+ *  - "Bridging the Gap Between Promise and Performance for Microscaling FP4
+ *    Quantization": "Probleemstelling" (group size 32, power-of-two E8M0
+ *    scales), "Methodologie: MR-GPTQ" item 1 (block-wise Hadamard on weights
+ *    and activations), "GPU Kernel Ondersteuning (QuTLASS)" (the rotation runs
+ *    online inside the quantization kernel).
+ *  - "KroQuant: Effiziente Post-Training-Quantisierung fuer Diffusion
+ *    Transformers mittels Kronecker-Produkt-Struktur": abstract and
+ *    "Tiefenanalyse" (learned Kronecker-structured transform on each
+ *    32-element activation block), "Hintergrund" (the inverse transform goes
+ *    on the weights, offline).
+ *
+ * Conventions shared by every entry point:
+ *  - Device pointers are HIP device memory owned by the caller; the library
+ *    allocates nothing and keeps no mutable global state (calls are
+ *    re-entrant).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Device work is
+ *    enqueued on it and the call returns without synchronizing; device faults
+ *    surface at the caller's next synchronization, as usual in HIP.
+ *  - Argument checks are synchronous and nothing is launched when they fail.
+ *    No exception crosses the ABI and the library never aborts.
+ *
+ * Packed layouts (row-major, K contiguous -- "K-major" for both operands):
+ *  - codes [rows][K/2] uint8: element 2j of a row in the low nibble of byte j,
+ *    element 2j+1 in the high nibble.  E2M1 code = sign<<3 | magnitude index
+ *    into {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *  - scales [rows][K/32] uint8: E8M0 byte s of block b means 2^(s-127).
+ *  Both are dense (row strides K/2 and K/32 bytes).
+ *
+ * Quantizer rule (per 32-block, after the optional rotation, all in fp32):
+ *  amax = max |y_i|;  e = max(floor(log2 amax) - 2, -127), e = -127 for
+ *  amax = 0;  scale byte = e + 127;  code_i = sign(y_i) | RNE-saturating
+ *  E2M1 index of |y_i| * 2^-e (ties to the even mantissa, > 6 saturates to 6;
+ *  the sign bit is kept for values that round to zero).
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(_WIN32)
+#define MXFP4_API
+#else
+#define MXFP4_API __attribute__((visibility("default")))
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum {
+    MXFP4_OK = 0,
+    MXFP4_ERR_INVALID_ARG = 1,  /* null pointer, bad size/stride, bad enum */
+    MXFP4_ERR_UNSUPPORTED = 2,  /* valid request this build does not run
+                                   (misaligned pointer, size beyond limits) */
+    MXFP4_ERR_HIP = 3           /* a HIP runtime call or launch failed */
+} mxfp4_status;
+
+/* Element types of dense inputs and outputs. */
+typedef enum {
+    MXFP4_F32 = 0,
+    MXFP4_BF16 = 1
+} mxfp4_dtype;
+
+/* Block rotation applied before quantization. */
+typedef enum {
+    MXFP4_ROT_NONE = 0,        /* plain MXFP4 round-to-nearest */
+    MXFP4_ROT_HADAMARD32 = 1,  /* y = H32 x / sqrt(32), Sylvester order */
+    MXFP4_ROT_KRON = 2         /* y = (A (x) B) x, A p x p, B q x q, p*q=32 */
+} mxfp4_rot_kind;
+
+/* Rotation descriptor (host struct; read during the call).
+ * HADAMARD32 evaluation order (fp32, no fused ops): butterflies
+ *   (u, v) -> (u + v, u - v) with strides 1, 2, 4, 8, 16, then a multiply by
+ *   fp32(1/sqrt(32)) = 0x3E3504F3.
+ * KRON evaluation order: with Xm[j][l] = x[q*j + l],
+ *   U[j][k] = chain_l B[k][l] * Xm[j][l],  y[q*i + k] = chain_j A[i][j] * U[j][k],
+ *   where a chain is the rounded first product followed by fused
+ *   multiply-adds in ascending index order.  */
+typedef struct {
+    int32_t kind;      /* mxfp4_rot_kind */
+    int32_t p;         /* KRON: rows of A (1, 2, 4, 8, 16 or 32) */
+    int32_t q;         /* KRON: rows of B, p * q == 32 */
+    int32_t reserved;  /* must be 0 */
+    const float* a;    /* KRON: device pointer, p*p fp32 row-major */
+    const float* b;    /* KRON: device pointer, q*q fp32 row-major */
+} mxfp4_rotation;
+
+/* Online quantization of a dense matrix to MXFP4 (with optional rotation).
+ *   x       device, [rows][ld_x] elements of x_dtype (F32 or BF16); the first
+ *           k columns of each row are quantized.  16-byte aligned, and ld_x a
+ *           multiple of 8 (BF16) or 4 (F32), else MXFP4_ERR_UNSUPPORTED.
+ *   rows    >= 0 (0 is a no-op);  k > 0, multiple of 32;  ld_x >= k.
+ *   rot     NULL or kind NONE: no rotation.
+ *   codes   device, [rows][k/2] bytes, 16-byte aligned (written).
+ *   scales  device, [rows][k/32] bytes (written).
+ * Errors: INVALID_ARG for null pointers (when rows > 0), k % 32 != 0, k <= 0,
+ *   rows < 0, ld_x < k, bad dtype, bad rotation (unknown kind, p*q != 32,
+ *   null factor pointers); UNSUPPORTED for misalignment or
+ *   rows * k / 32 >= 2^31; HIP if the launch fails. */
+MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype,
+                                             int64_t rows, int64_t k, int64_t ld_x,
+                                             const mxfp4_rotation* rot,
+                                             uint8_t* codes, uint8_t* scales,
+                                             void* stream);
+
+/* Y = A * B^T on MXFP4 operands, fp32 accumulation.
+ *   a_codes/a_scales  device, A in the packed layout above, m rows.
+ *   b_codes/b_scales  device, B in the packed layout above, n rows
+ *                     (for a linear layer B = W, [out_features][in_features]).
+ *   m, n >= 0 (0 is a no-op), k > 0 multiple of 32.
+ *   y       device, [m][ld_y] elements of y_dtype (F32 or BF16), ld_y >= n;
+ *           element (i, j) = sum over blocks of 2^(sa-127) 2^(sb-127) times
+ *           the block's E2M1 dot product, accumulated in fp32, rounded to
+ *           bf16 (nearest-even) for BF16 output.
+ *   Code pointers 16-byte aligned.
+ * Errors: INVALID_ARG for null pointers (when m, n > 0), k % 32 != 0, k <= 0,
+ *   negative sizes, ld_y < n, bad dtype; UNSUPPORTED for misaligned code
+ *   pointers or m, n, k >= 2^30; HIP if the launch fails. */
+MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
+                                  const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
+                                  int64_t k, void* y, int32_t y_dtype, int64_t ld_y,
+                                  void* stream);
+
+/* Host helper for the offline weight fold of a Kronecker transform: since
+ * (A (x) B)^-T = A^-T (x) B^-T, quantizing the weights with KRON factors
+ * (A^-T, B^-T) keeps every block dot product (T x) . (T^-T w) = x . w.
+ *   m    host, n x n fp32 row-major;  out  host, n x n fp32 (written);
+ *   1 <= n <= 32.  Binary64 Gauss-Jordan with partial pivoting, then
+ *   transposed and rounded to fp32.
+ * Errors: INVALID_ARG for null pointers or n out of range, or a singular
+ *   matrix (a zero pivot). */
+MXFP4_API mxfp4_status mxfp4_inverse_transpose(const float* m, int32_t n, float* out);
+
+/* Static description of a status code (never NULL). */
+MXFP4_API const char* mxfp4_status_string(int32_t status);
+
+/* ABI version of this header (bumped on incompatible changes). */
+#define MXFP4_ABI_VERSION 1
+MXFP4_API int32_t mxfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

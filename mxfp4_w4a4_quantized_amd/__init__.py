@@ -1,0 +1,208 @@
+"""W4A4 MXFP4 linear layer for MI355X (gfx950): a thin binding over libmxfp4.so.
+
+Every step of the layer runs in the HIP library's kernels; this module only
+marshals torch tensors (device memory and the current HIP stream) into the
+C-ABI calls declared in include/mxfp4.h:
+
+  quantize_rotate(x, rot)            online MXFP4 quantization of activations,
+                                     with an optional per-32-block rotation
+  gemm(a_codes, a_scales, b_codes, b_scales, out_dtype)
+                                     Y = A * B^T on packed MXFP4 operands
+  linear(x, w_codes, w_scales, rot)  the two above, back to back
+  quantize_weight(w, rot)            offline weight quantization with the
+                                     weight side of the rotation
+  inverse_transpose(m)               host helper for the Kronecker weight fold
+
+Rotations: None, HADAMARD32, or Kron(a, b) -- a learned Kronecker-factored
+32x32 transform A (x) B ("KroQuant: ...", abstract and "Tiefenanalyse"); the
+Hadamard-32 is the MR-GPTQ block rotation ("Bridging the Gap Between Promise
+and Performance for Microscaling FP4 Quantization", "Methodologie: MR-GPTQ").
+
+There is no fallback: if the library is missing, importing works but every
+call raises.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxfp4.so")
+
+MXFP4_OK, MXFP4_ERR_INVALID_ARG, MXFP4_ERR_UNSUPPORTED, MXFP4_ERR_HIP = 0, 1, 2, 3
+MXFP4_F32, MXFP4_BF16 = 0, 1
+ROT_NONE, ROT_HADAMARD32, ROT_KRON = 0, 1, 2
+
+HADAMARD32 = "h32"
+
+EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_gemm", "mxfp4_inverse_transpose",
+            "mxfp4_status_string", "mxfp4_abi_version")
+
+
+class Mxfp4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+class RotationDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("p", ctypes.c_int32), ("q", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(the MXFP4 path has no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.mxfp4_quantize_rotate.restype = i32
+    L.mxfp4_quantize_rotate.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), vp, vp, vp]
+    L.mxfp4_gemm.restype = i32
+    L.mxfp4_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i32, i64, vp]
+    L.mxfp4_inverse_transpose.restype = i32
+    L.mxfp4_inverse_transpose.argtypes = [vp, i32, vp]
+    L.mxfp4_status_string.restype = ctypes.c_char_p
+    L.mxfp4_status_string.argtypes = [i32]
+    L.mxfp4_abi_version.restype = i32
+    L.mxfp4_abi_version.argtypes = []
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().mxfp4_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != MXFP4_OK:
+        raise Mxfp4Error(status, what)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclass
+class Kron:
+    """Kronecker-factored block transform T = A (x) B (A p x p, B q x q,
+    p*q = 32), factors as fp32 device tensors."""
+    a: torch.Tensor
+    b: torch.Tensor
+
+    @staticmethod
+    def from_host(a: np.ndarray, b: np.ndarray, device="cuda") -> "Kron":
+        return Kron(torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device),
+                    torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(device))
+
+    def weight_side(self) -> "Kron":
+        """Factors (A^-T, B^-T) of T^-T, for folding the inverse into W."""
+        a = inverse_transpose(self.a.cpu().numpy())
+        b = inverse_transpose(self.b.cpu().numpy())
+        return Kron.from_host(a, b, self.a.device)
+
+
+def _rot_desc(rot, device):
+    if rot is None:
+        return None, ()
+    if isinstance(rot, str):
+        if rot != HADAMARD32:
+            raise ValueError(f"unknown rotation {rot!r}")
+        return RotationDesc(ROT_HADAMARD32, 0, 0, 0, None, None), ()
+    if isinstance(rot, Kron):
+        a, b = rot.a, rot.b
+        for t in (a, b):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.device != device:
+                raise ValueError("Kron factors must be contiguous fp32 tensors on the input's device")
+        return RotationDesc(ROT_KRON, a.shape[0], b.shape[0], 0, a.data_ptr(), b.data_ptr()), (a, b)
+    raise TypeError(f"bad rotation {rot!r}")
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.float32:
+        return MXFP4_F32
+    if dt == torch.bfloat16:
+        return MXFP4_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def quantize_rotate(x: torch.Tensor, rot=None, codes: torch.Tensor = None, scales: torch.Tensor = None):
+    """MXFP4-quantize the rows of x (fp32 or bf16, [rows, k], unit column
+    stride) with an optional block rotation.  Returns (codes [rows, k/2]
+    uint8, scales [rows, k/32] uint8)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, k = x.shape
+    if codes is None:
+        codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("codes and scales must be contiguous")
+    desc, _keep = _rot_desc(rot, x.device)
+    st = lib().mxfp4_quantize_rotate(
+        x.data_ptr(), _dtype_code(x.dtype), rows, k, x.stride(0),
+        ctypes.byref(desc) if desc is not None else None,
+        codes.data_ptr(), scales.data_ptr(), _stream(x.device))
+    _check(st, "mxfp4_quantize_rotate")
+    return codes, scales
+
+
+def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
+         out_dtype=torch.bfloat16, y: torch.Tensor = None) -> torch.Tensor:
+    """Y = A * B^T with A [m, k] and B [n, k] in packed MXFP4 (codes [*, k/2],
+    scales [*, k/32]); fp32 accumulation, fp32 or bf16 output [m, n]."""
+    m, n, k = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != k or a_scales.shape != (m, k // 32) or b_scales.shape != (n, k // 32):
+        raise ValueError("operand shapes disagree")
+    for t in (a_codes, a_scales, b_codes, b_scales):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("codes and scales must be contiguous uint8 tensors")
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
+    if y.dim() != 2 or y.shape != (m, n) or y.stride(1) != 1:
+        raise ValueError("y must be [m, n] with unit column stride")
+    st = lib().mxfp4_gemm(a_codes.data_ptr(), a_scales.data_ptr(), m,
+                          b_codes.data_ptr(), b_scales.data_ptr(), n, k,
+                          y.data_ptr(), _dtype_code(y.dtype), y.stride(0), _stream(a_codes.device))
+    _check(st, "mxfp4_gemm")
+    return y
+
+
+def linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, rot=None,
+           out_dtype=torch.bfloat16, y: torch.Tensor = None) -> torch.Tensor:
+    """One W4A4 MXFP4 linear layer: online quantization of x (with the
+    activation side of `rot`) followed by the MXFP4 GEMM against
+    pre-quantized weights."""
+    a_codes, a_scales = quantize_rotate(x, rot)
+    return gemm(a_codes, a_scales, w_codes, w_scales, out_dtype, y)
+
+
+def quantize_weight(w: torch.Tensor, rot=None):
+    """Offline weight quantization with the weight side of `rot`: the same
+    Hadamard-32 (it is its own inverse-transpose), or the Kronecker factors
+    (A^-T, B^-T), so that each block dot product is preserved."""
+    if isinstance(rot, Kron):
+        rot = rot.weight_side()
+    return quantize_rotate(w, rot)
+
+
+def inverse_transpose(m: np.ndarray) -> np.ndarray:
+    """M^-T rounded to fp32 (binary64 elimination in the library)."""
+    m = np.ascontiguousarray(m, dtype=np.float32)
+    n = m.shape[0]
+    if m.shape != (n, n):
+        raise ValueError("square matrix expected")
+    out = np.empty((n, n), np.float32)
+    st = lib().mxfp4_inverse_transpose(m.ctypes.data, n, out.ctypes.data)
+    _check(st, "mxfp4_inverse_transpose")
+    return out

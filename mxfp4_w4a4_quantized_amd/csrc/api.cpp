@@ -1,0 +1,136 @@
+// C-ABI layer: argument validation, kernel selection, HIP error mapping.
+// The declarations, layouts and error behaviour are documented in mxfp4.h.
+#include "mxfp4.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+mxfp4_status from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+}  // namespace
+
+extern "C" {
+
+MXFP4_API int32_t mxfp4_abi_version(void) { return MXFP4_ABI_VERSION; }
+
+MXFP4_API const char* mxfp4_status_string(int32_t status) {
+  switch (status) {
+    case MXFP4_OK: return "MXFP4_OK";
+    case MXFP4_ERR_INVALID_ARG: return "MXFP4_ERR_INVALID_ARG: invalid argument";
+    case MXFP4_ERR_UNSUPPORTED: return "MXFP4_ERR_UNSUPPORTED: unsupported alignment or size";
+    case MXFP4_ERR_HIP: return "MXFP4_ERR_HIP: HIP runtime or launch failure";
+    default: return "MXFP4: unknown status";
+  }
+}
+
+MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype, int64_t rows, int64_t k,
+                                             int64_t ld_x, const mxfp4_rotation* rot,
+                                             uint8_t* codes, uint8_t* scales, void* stream) {
+  if (x_dtype != MXFP4_F32 && x_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
+  if (rows < 0 || k <= 0 || (k % 32) != 0 || ld_x < k) return MXFP4_ERR_INVALID_ARG;
+  int32_t kind = MXFP4_ROT_NONE, p = 0, q = 0;
+  const float *fa = nullptr, *fb = nullptr;
+  if (rot != nullptr) {
+    kind = rot->kind;
+    if (kind != MXFP4_ROT_NONE && kind != MXFP4_ROT_HADAMARD32 && kind != MXFP4_ROT_KRON)
+      return MXFP4_ERR_INVALID_ARG;
+    if (rot->reserved != 0) return MXFP4_ERR_INVALID_ARG;
+    if (kind == MXFP4_ROT_KRON) {
+      p = rot->p;
+      q = rot->q;
+      if (p < 1 || q < 1 || p * q != 32 || (p & (p - 1)) != 0) return MXFP4_ERR_INVALID_ARG;
+      if (rot->a == nullptr || rot->b == nullptr) return MXFP4_ERR_INVALID_ARG;
+      fa = rot->a;
+      fb = rot->b;
+      if (!aligned(fa, 4) || !aligned(fb, 4)) return MXFP4_ERR_UNSUPPORTED;
+    }
+  }
+  if (rows == 0) return MXFP4_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MXFP4_ERR_INVALID_ARG;
+  const int64_t elem = (x_dtype == MXFP4_BF16) ? 2 : 4;
+  if (!aligned(x, 16) || ((ld_x * elem) % 16) != 0 || !aligned(codes, 16)) return MXFP4_ERR_UNSUPPORTED;
+  if (rows * (k / 32) >= (int64_t(1) << 31)) return MXFP4_ERR_UNSUPPORTED;
+
+  mxfp4::QuantArgs a;
+  a.x = x;
+  a.ld_x = ld_x;
+  a.rows = static_cast<uint32_t>(rows);
+  a.nblk_row = static_cast<uint32_t>(k / 32);
+  a.rot = kind;
+  a.p = p;
+  a.q = q;
+  a.fa = fa;
+  a.fb = fb;
+  a.codes = codes;
+  a.scales = scales;
+  return from_hip(mxfp4::launch_quantize(a, x_dtype == MXFP4_BF16, static_cast<hipStream_t>(stream)));
+}
+
+MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
+                                  const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, int64_t k,
+                                  void* y, int32_t y_dtype, int64_t ld_y, void* stream) {
+  if (y_dtype != MXFP4_F32 && y_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
+  if (m < 0 || n < 0 || k <= 0 || (k % 32) != 0 || ld_y < n) return MXFP4_ERR_INVALID_ARG;
+  if (m == 0 || n == 0) return MXFP4_OK;
+  if (a_codes == nullptr || a_scales == nullptr || b_codes == nullptr || b_scales == nullptr ||
+      y == nullptr)
+    return MXFP4_ERR_INVALID_ARG;
+  if (m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return MXFP4_ERR_UNSUPPORTED;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return MXFP4_ERR_UNSUPPORTED;
+  const int64_t ybytes = (y_dtype == MXFP4_BF16) ? 2 : 4;
+  if (!aligned(y, ybytes)) return MXFP4_ERR_UNSUPPORTED;
+
+  mxfp4::GemmArgs g;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.b_codes = b_codes;
+  g.b_scales = b_scales;
+  g.m = static_cast<int32_t>(m);
+  g.n = static_cast<int32_t>(n);
+  g.k = static_cast<int32_t>(k);
+  g.y = y;
+  g.ld_y = ld_y;
+  g.y_bf16 = (y_dtype == MXFP4_BF16);
+  return from_hip(mxfp4::launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+// Binary64 Gauss-Jordan elimination with partial pivoting on [M | I]; the
+// right half becomes M^-1, which is written transposed and rounded to fp32.
+MXFP4_API mxfp4_status mxfp4_inverse_transpose(const float* m, int32_t n, float* out) {
+  if (m == nullptr || out == nullptr || n < 1 || n > 32) return MXFP4_ERR_INVALID_ARG;
+  double t[32][64];
+  for (int r = 0; r < n; ++r)
+    for (int c = 0; c < 2 * n; ++c) t[r][c] = (c < n) ? double(m[r * n + c]) : (c - n == r ? 1.0 : 0.0);
+  for (int col = 0; col < n; ++col) {
+    int piv = col;
+    for (int r = col + 1; r < n; ++r)
+      if (std::fabs(t[r][col]) > std::fabs(t[piv][col])) piv = r;
+    if (t[piv][col] == 0.0) return MXFP4_ERR_INVALID_ARG;
+    if (piv != col)
+      for (int c = 0; c < 2 * n; ++c) {
+        const double s = t[col][c];
+        t[col][c] = t[piv][c];
+        t[piv][c] = s;
+      }
+    const double d = t[col][col];
+    for (int c = 0; c < 2 * n; ++c) t[col][c] /= d;
+    for (int r = 0; r < n; ++r) {
+      if (r == col || t[r][col] == 0.0) continue;
+      const double f = t[r][col];
+      for (int c = 0; c < 2 * n; ++c) t[r][c] -= f * t[col][c];
+    }
+  }
+  for (int r = 0; r < n; ++r)
+    for (int c = 0; c < n; ++c) out[r * n + c] = static_cast<float>(t[c][n + r]);
+  return MXFP4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the HIP
+// kernels.  Arguments reaching these functions are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mxfp4 {
+
+struct QuantArgs {
+  const void* x;
+  int64_t ld_x;        // elements
+  uint32_t rows;
+  uint32_t nblk_row;   // k / 32
+  int32_t rot;         // mxfp4_rot_kind
+  int32_t p, q;        // Kronecker factor sizes
+  const float* fa;     // p x p
+  const float* fb;     // q x q
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, bool bf16, hipStream_t s);
+
+struct GemmArgs {
+  const uint8_t* a_codes;   // X side, m rows
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;   // W side, n rows
+  const uint8_t* b_scales;
+  int32_t m, n, k;
+  void* y;
+  int64_t ld_y;
+  bool y_bf16;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace mxfp4

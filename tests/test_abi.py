@@ -1,0 +1,124 @@
+"""Boundary checks that need no GPU: the library loads, exports every symbol
+include/mxfp4.h declares, and rejects bad arguments synchronously (before any
+device work).  The host-side Kronecker fold helper is compared with the
+oracle's.  No compute call reaches the device here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mxfp4_w4a4_quantized_amd as mx
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+NULL = None
+ALIGNED = 1 << 20          # arbitrary aligned address: never dereferenced
+MISALIGNED = ALIGNED + 4
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MXFP4_API\s+[\w\s\*]+?\b(mxfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    assert syms == sorted(mx.EXPORTED)
+    assert {"mxfp4_quantize_rotate", "mxfp4_gemm"} <= set(syms)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = mx.lib()
+    for s in declared_symbols():
+        assert hasattr(L, s), s
+    out = os.popen(f"nm -D --defined-only {mx.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT (mxfp4_\w+)", out))
+    assert exported == set(declared_symbols())
+
+
+def test_abi_version_and_status_strings():
+    assert mx.lib().mxfp4_abi_version() == 1
+    for s in range(4):
+        assert mx.status_string(s).startswith("MXFP4_")
+    assert "unknown" in mx.status_string(99)
+
+
+def q(*args):
+    return mx.lib().mxfp4_quantize_rotate(*args)
+
+
+def g(*args):
+    return mx.lib().mxfp4_gemm(*args)
+
+
+def test_quantize_argument_errors():
+    INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
+    A = ALIGNED
+    assert q(A, 7, 4, 64, 64, None, A, A, None) == INV      # bad dtype
+    assert q(A, 1, 4, 48, 64, None, A, A, None) == INV      # k % 32
+    assert q(A, 1, 4, 0, 64, None, A, A, None) == INV       # k == 0
+    assert q(A, 1, -1, 64, 64, None, A, A, None) == INV     # rows < 0
+    assert q(A, 1, 4, 64, 32, None, A, A, None) == INV      # ld < k
+    assert q(NULL, 1, 4, 64, 64, None, A, A, None) == INV   # null x
+    assert q(A, 1, 4, 64, 64, None, NULL, A, None) == INV   # null codes
+    assert q(A, 1, 4, 64, 64, None, A, NULL, None) == INV   # null scales
+    assert q(NULL, 1, 0, 64, 64, None, NULL, NULL, None) == OK   # rows == 0: no-op
+    assert q(MISALIGNED, 1, 4, 64, 64, None, A, A, None) == UNS
+    assert q(A, 1, 4, 64, 68, None, A, A, None) == UNS      # bf16 row stride not 16 B
+    assert q(A, 1, 4, 64, 64, None, A + 8, A, None) == UNS  # codes not 16 B aligned
+    assert q(A, 1, 1 << 30, 4096, 4096, None, A, A, None) == UNS   # too many blocks
+    bad = mx.RotationDesc(9, 0, 0, 0, None, None)
+    assert q(A, 1, 4, 64, 64, ctypes.byref(bad), A, A, None) == INV
+    kr = mx.RotationDesc(mx.ROT_KRON, 4, 4, 0, A, A)
+    assert q(A, 1, 4, 64, 64, ctypes.byref(kr), A, A, None) == INV     # p*q != 32
+    kr = mx.RotationDesc(mx.ROT_KRON, 4, 8, 0, None, A)
+    assert q(A, 1, 4, 64, 64, ctypes.byref(kr), A, A, None) == INV     # null factor
+    kr = mx.RotationDesc(mx.ROT_KRON, 4, 8, 1, A, A)
+    assert q(A, 1, 4, 64, 64, ctypes.byref(kr), A, A, None) == INV     # reserved != 0
+
+
+def test_gemm_argument_errors():
+    INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
+    A = ALIGNED
+    assert g(A, A, 4, A, A, 4, 64, A, 5, 4, None) == INV     # bad dtype
+    assert g(A, A, 4, A, A, 4, 48, A, 0, 4, None) == INV     # k % 32
+    assert g(A, A, 4, A, A, 4, 0, A, 0, 4, None) == INV      # k == 0
+    assert g(A, A, -4, A, A, 4, 64, A, 0, 4, None) == INV    # m < 0
+    assert g(A, A, 4, A, A, -4, 64, A, 0, 4, None) == INV    # n < 0
+    assert g(A, A, 4, A, A, 8, 64, A, 0, 4, None) == INV     # ld_y < n
+    assert g(NULL, A, 4, A, A, 4, 64, A, 0, 4, None) == INV
+    assert g(A, NULL, 4, A, A, 4, 64, A, 0, 4, None) == INV
+    assert g(A, A, 4, NULL, A, 4, 64, A, 0, 4, None) == INV
+    assert g(A, A, 4, A, NULL, 4, 64, A, 0, 4, None) == INV
+    assert g(A, A, 4, A, A, 4, 64, NULL, 0, 4, None) == INV
+    assert g(NULL, NULL, 0, NULL, NULL, 4, 64, NULL, 0, 4, None) == OK   # m == 0
+    assert g(NULL, NULL, 4, NULL, NULL, 0, 64, NULL, 0, 0, None) == OK   # n == 0
+    assert g(A + 4, A, 4, A, A, 4, 64, A, 0, 4, None) == UNS   # misaligned codes
+    assert g(A, A, 4, A + 8, A, 4, 64, A, 0, 4, None) == UNS
+    assert g(A, A, 4, A, A, 4, 64, A + 2, 0, 4, None) == UNS   # fp32 y misaligned
+    assert g(A, A, 1 << 30, A, A, 4, 64, A, 0, 4, None) == UNS
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32])
+def test_inverse_transpose_matches_oracle(n):
+    rng = np.random.default_rng(40 + n)
+    m = (np.eye(n) + 0.1 * rng.standard_normal((n, n))).astype(np.float32)
+    got = mx.inverse_transpose(m)
+    ref = oracle.inverse_transpose(m)
+    # both round a binary64 inverse to fp32: equal, or one ulp apart where the
+    # binary64 results straddle an fp32 rounding boundary
+    ulp = np.spacing(np.abs(ref))
+    assert np.all(np.abs(got - ref) <= ulp)
+    assert np.mean(got == ref) > 0.99
+
+
+def test_inverse_transpose_errors():
+    with pytest.raises(mx.Mxfp4Error):
+        mx.inverse_transpose(np.zeros((4, 4), np.float32))      # singular
+    assert mx.lib().mxfp4_inverse_transpose(None, 4, None) == mx.MXFP4_ERR_INVALID_ARG
+    m = np.eye(4, dtype=np.float32)
+    assert mx.lib().mxfp4_inverse_transpose(m.ctypes.data, 33, m.ctypes.data) == mx.MXFP4_ERR_INVALID_ARG

@@ -1,0 +1,229 @@
+"""GPU parity of the MXFP4 GEMM against the oracle's binary64 GEMM.
+
+Tolerance (fp32 output): for every checked element,
+    |Y_gpu - Y_oracle| <= 1e-5 * ||a_hat_m||_2 * ||b_hat_n||_2.
+Derivation: inside one 32-element block every product of two E2M1 values is
+a multiple of 1/4 below 36 in magnitude and the block sum is exact; the
+kernel's only roundings are the fp32 accumulations across K (at most K/32 of
+them, each with relative error 2^-24) and the block scaling, so the error is
+below (K/32 + 1) * 2^-24 * sum_k |a_hat b_hat| <= (K/32 + 1) * 2^-24 *
+||a_hat|| ||b_hat|| (Cauchy-Schwarz) -- 2.3e-5 in the worst case at
+K = 12288, ~1e-6 in practice since the rounding errors do not align.
+bf16 output: Y_bf16 must equal the round-to-nearest-even bf16 of the same
+kernel's fp32 output bit for bit, and lie within half a bf16 ulp of the
+oracle plus the fp32 bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_w4a4_quantized_amd as mx
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 1e-5
+
+
+def announce(*what):
+    print("[case]", *what, flush=True)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def row_norms(codes, scales):
+    return np.sqrt((oracle.dequantize(codes, scales) ** 2).sum(axis=1))
+
+
+def norm_err(got, ref, na, nb):
+    den = np.outer(na, nb) if got.ndim == 2 else na * nb
+    diff = np.abs(got.astype(np.float64) - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(den > 0, diff / den, np.where(diff == 0, 0.0, np.inf))
+    return float(rel.max()) if rel.size else 0.0
+
+
+def bf16_rne(y32: torch.Tensor) -> np.ndarray:
+    return y32.to(torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_both(ac, as_, bc, bs):
+    dac, das, dbc, dbs = map(to_dev, (ac, as_, bc, bs))
+    y32 = mx.gemm(dac, das, dbc, dbs, torch.float32)
+    y16 = mx.gemm(dac, das, dbc, dbs, torch.bfloat16)
+    torch.cuda.synchronize()
+    return y32, y16
+
+
+def check_full(ac, as_, bc, bs, what):
+    m, n = ac.shape[0], bc.shape[0]
+    announce("gemm", what, m, n, ac.shape[1] * 2)
+    y32, y16 = run_both(ac, as_, bc, bs)
+    ref = oracle.gemm(ac, as_, bc, bs)
+    na, nb = row_norms(ac, as_), row_norms(bc, bs)
+    err = norm_err(y32.cpu().numpy(), ref, na, nb)
+    assert err <= TOL, f"{what}: normalized error {err:.3e}"
+    # bf16 epilogue: RNE of the same fp32 result
+    assert np.array_equal(y16.view(torch.int16).cpu().numpy().view(np.uint16), bf16_rne(y32))
+    yb = y16.float().cpu().numpy().astype(np.float64)
+    half_ulp = np.abs(ref) * 2.0 ** -8 + 1e-300
+    assert np.all(np.abs(yb - ref) <= half_ulp + TOL * np.outer(na, nb) + 1e-300)
+    return err
+
+
+# ------------------------------------------------------------ small cases ---
+
+SHAPES = [
+    (1, 1, 32), (16, 16, 128), (128, 128, 256), (17, 33, 96), (130, 260, 544),
+    (257, 129, 1056), (300, 500, 2048), (64, 640, 4096), (5, 1000, 320),
+]
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_random_operands(m, n, k):
+    rng = np.random.default_rng(m * 131 + n * 7 + k)
+    ac, as_ = workloads.random_mxfp4(rng, m, k)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+    check_full(ac, as_, bc, bs, "random")
+
+
+def test_extreme_scales():
+    # scale bytes near both ends of the E8M0 range (products stay finite)
+    rng = np.random.default_rng(77)
+    m, n, k = 48, 80, 512
+    ac, _ = workloads.random_mxfp4(rng, m, k)
+    bc, _ = workloads.random_mxfp4(rng, n, k)
+    as_ = rng.integers(0, 40, (m, k // 32)).astype(np.uint8)        # 2^-127 .. 2^-88
+    bs = rng.integers(200, 254, (n, k // 32)).astype(np.uint8)      # 2^73 .. 2^126
+    check_full(ac, as_, bc, bs, "extreme scales")
+
+
+def test_zero_and_sign_codes():
+    rng = np.random.default_rng(78)
+    m, n, k = 40, 72, 256
+    ac = np.full((m, k // 2), 0x88, np.uint8)                         # all -0
+    ac[::3] = rng.integers(0, 256, (len(ac[::3]), k // 2), dtype=np.uint8)
+    as_ = np.full((m, k // 32), 127, np.uint8)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+    check_full(ac, as_, bc, bs, "zeros")
+
+
+def test_strided_output():
+    rng = np.random.default_rng(79)
+    m, n, k = 70, 90, 384
+    ac, as_ = workloads.random_mxfp4(rng, m, k)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+    big = torch.full((m, n + 38), 7.0, dtype=torch.float32, device=DEV)
+    y = big[:, 5:5 + n]                                                # ld_y = n + 38, offset 5
+    announce("gemm strided", m, n, k)
+    mx.gemm(*map(to_dev, (ac, as_, bc, bs)), torch.float32, y=y)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(ac, as_, bc, bs)
+    err = norm_err(y.cpu().numpy(), ref, row_norms(ac, as_), row_norms(bc, bs))
+    assert err <= TOL
+    host = big.cpu().numpy()
+    assert (host[:, :5] == 7.0).all() and (host[:, 5 + n:] == 7.0).all()   # no stray writes
+
+
+def test_empty_gemm_is_noop():
+    z = torch.empty((0, 16), dtype=torch.uint8, device=DEV)
+    zs = torch.empty((0, 1), dtype=torch.uint8, device=DEV)
+    b = torch.zeros((8, 16), dtype=torch.uint8, device=DEV)
+    bs = torch.zeros((8, 1), dtype=torch.uint8, device=DEV)
+    y = mx.gemm(z, zs, b, bs, torch.float32)
+    assert y.shape == (0, 8)
+
+
+# -------------------------------------------------- linear layer, tiny ---
+
+def test_tiny_linear_end_to_end():
+    """The tiny workload end to end: both operands quantized on the device
+    (bit-exact vs the oracle), then the GEMM checked on every element."""
+    inp = workloads.make("tiny")
+    x = to_dev(inp["x"])
+    w = to_dev(inp["w"])
+    wc, ws = mx.quantize_weight(w)
+    xc, xs = mx.quantize_rotate(x)
+    y = mx.gemm(xc, xs, wc, ws, torch.float32)
+    yl = mx.linear(x, wc, ws, None, torch.float32)
+    torch.cuda.synchronize()
+    rxc, rxs = oracle.quantize(inp["x"])
+    rwc, rws = oracle.quantize(inp["w"])
+    assert np.array_equal(xc.cpu().numpy(), rxc) and np.array_equal(xs.cpu().numpy(), rxs)
+    assert np.array_equal(wc.cpu().numpy(), rwc) and np.array_equal(ws.cpu().numpy(), rws)
+    ref = oracle.gemm(rxc, rxs, rwc, rws)
+    err = norm_err(y.cpu().numpy(), ref, row_norms(rxc, rxs), row_norms(rwc, rws))
+    assert err <= TOL
+    assert torch.equal(y, yl)
+
+
+# --------------------------------------------------------- full workloads ---
+
+def act_rot(inp):
+    wl = inp["wl"]
+    if wl.rot == "h32":
+        return "h32"
+    if wl.rot == "kron":
+        return mx.Kron.from_host(inp["a"], inp["b"], DEV)
+    return None
+
+
+@pytest.mark.parametrize("name", [n for n in workloads.WORKLOADS if n != "tiny"])
+def test_full_workload_linear(name):
+    """Full-size linear layer in the launch configuration the benchmark
+    times: device quantization of X (activation side) and W (weight side),
+    then the GEMM; operands checked bit-exact against the oracle's, outputs
+    checked on 4096 sampled elements plus the whole first and last rows and
+    columns, with the oracle computing each sampled element as one binary64
+    dot product."""
+    inp = workloads.make(name)
+    wl = inp["wl"]
+    bf16 = wl.x_dtype == "bf16"
+    x = to_dev(inp["x"].view(np.int16)).view(torch.bfloat16) if bf16 else to_dev(inp["x"])
+    w = to_dev(inp["w"])
+    rot = act_rot(inp)
+    announce("linear", name, wl.m, wl.n, wl.k)
+    wc, ws = mx.quantize_weight(w, rot)
+    out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+    xc, xs = mx.quantize_rotate(x, rot)
+    y32 = mx.gemm(xc, xs, wc, ws, torch.float32)
+    y = mx.gemm(xc, xs, wc, ws, out_dtype)
+    torch.cuda.synchronize()
+    hxc, hxs, hwc, hws = (t.cpu().numpy() for t in (xc, xs, wc, ws))
+    # operands: bit-exact against the oracle's quantizer
+    orot = None if wl.rot is None else ("h32" if wl.rot == "h32" else ("kron", inp["a"], inp["b"]))
+    rxc, rxs = oracle.quantize(inp["x"], rot=orot, bf16=bf16)
+    assert np.array_equal(hxc, rxc) and np.array_equal(hxs, rxs)
+    if wl.rot == "kron":
+        # weight side: the library's A^-T, B^-T (checked against the oracle's
+        # in the ABI tests), applied by the oracle's quantizer
+        wr = rot.weight_side()
+        worot = ("kron", wr.a.cpu().numpy(), wr.b.cpu().numpy())
+    else:
+        worot = orot
+    rwc, rws = oracle.quantize(inp["w"], rot=worot)
+    assert np.array_equal(hwc, rwc) and np.array_equal(hws, rws)
+    # outputs at sampled points
+    rng = np.random.default_rng(1)
+    m, n = wl.m, wl.n
+    mi = np.concatenate([rng.integers(0, m, 4096), np.zeros(n, np.int64), np.full(n, m - 1),
+                         np.arange(m), np.arange(m)])
+    ni = np.concatenate([rng.integers(0, n, 4096), np.arange(n), np.arange(n),
+                         np.zeros(m, np.int64), np.full(m, n - 1)])
+    ref = oracle.gemm_entries(hxc, hxs, hwc, hws, mi, ni)
+    na = row_norms(hxc[np.unique(mi)], hxs[np.unique(mi)])
+    nmap_a = dict(zip(np.unique(mi), na))
+    nb = row_norms(hwc[np.unique(ni)], hws[np.unique(ni)])
+    nmap_b = dict(zip(np.unique(ni), nb))
+    den_a = np.array([nmap_a[i] for i in mi])
+    den_b = np.array([nmap_b[j] for j in ni])
+    g32 = y32[torch.from_numpy(mi).to(DEV), torch.from_numpy(ni).to(DEV)].cpu().numpy()
+    err = norm_err(g32, ref, den_a, den_b)
+    print(f"[result] {name}: max normalized error {err:.3e}", flush=True)
+    assert err <= TOL
+    if out_dtype == torch.bfloat16:
+        assert torch.equal(y.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))

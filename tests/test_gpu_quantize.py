@@ -1,0 +1,158 @@
+"""GPU parity of the MXFP4 quantizer: codes and scales must equal the CPU
+oracle's bit for bit, on the same seeded inputs, for every rotation, input
+dtype, ragged size, strided input, edge block and full-size workload."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_w4a4_quantized_amd as mx
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def announce(*what):
+    print("[case]", *what, flush=True)
+
+
+def dev_x(x_host: np.ndarray, bf16: bool) -> torch.Tensor:
+    if bf16:
+        return torch.from_numpy(np.ascontiguousarray(x_host).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x_host, np.float32)).to(DEV)
+
+
+def gpu_quantize(x_host, bf16, rot=None):
+    x = dev_x(x_host, bf16)
+    c, s = mx.quantize_rotate(x, rot)
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), s.cpu().numpy()
+
+
+def oracle_rot(rot):
+    if rot is None or rot == "h32":
+        return rot
+    return ("kron", rot.a.cpu().numpy(), rot.b.cpu().numpy())
+
+
+def assert_same(got, ref, what):
+    gc, gs = got
+    rc, rs = ref
+    bad_s = np.count_nonzero(gs != rs)
+    bad_c = np.count_nonzero(gc != rc)
+    assert bad_s == 0 and bad_c == 0, f"{what}: {bad_s} scale bytes and {bad_c} code bytes differ"
+
+
+def check(x_host, bf16, rot=None, what=""):
+    announce("quantize", what, x_host.shape, "bf16" if bf16 else "f32", rot if isinstance(rot, str) else type(rot).__name__)
+    got = gpu_quantize(x_host, bf16, rot)
+    ref = oracle.quantize(x_host, rot=oracle_rot(rot), bf16=bf16)
+    assert_same(got, ref, what)
+
+
+def rand_kron(p, q, seed):
+    rng = np.random.default_rng(seed)
+    a = (np.eye(p) + 0.1 * rng.standard_normal((p, p))).astype(np.float32)
+    b = (np.eye(q) + 0.1 * rng.standard_normal((q, q))).astype(np.float32)
+    return mx.Kron.from_host(a, b, DEV)
+
+
+# ------------------------------------------------------------ small cases ---
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("rot", [None, "h32"])
+@pytest.mark.parametrize("rows,k", [(1, 32), (3, 96), (64, 256), (257, 544), (1000, 4096)])
+def test_random_blocks(rows, k, rot, bf16):
+    rng = np.random.default_rng(rows * 7 + k)
+    x = workloads.random_blocks(rng, rows, k)
+    if bf16:
+        x = workloads.bf16_bits(x)
+    check(x, bf16, rot, f"random {rows}x{k}")
+
+
+@pytest.mark.parametrize("p,q", [(1, 32), (2, 16), (4, 8), (8, 4), (16, 2), (32, 1)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_kron_all_factorizations(p, q, bf16):
+    rng = np.random.default_rng(p * 100 + q)
+    x = workloads.random_blocks(rng, 129, 320)
+    if bf16:
+        x = workloads.bf16_bits(x)
+    check(x, bf16, rand_kron(p, q, p + 17 * q), f"kron {p}x{q}")
+
+
+def edge_blocks(big: float = 3.0e38) -> np.ndarray:
+    """Edge blocks; `big` is the near-overflow magnitude (kept small enough
+    that a rotation's sums stay finite)."""
+    rows = []
+    z = np.zeros(32, np.float32)
+    rows.append(z.copy())                                        # all zero
+    rows.append(np.full(32, -0.0, np.float32))                   # all -0
+    rows.append(np.full(32, 1e-45, np.float32))                  # min subnormal
+    r = np.full(32, 2.0 ** -127, np.float32); r[3] = 2.0 ** -126; rows.append(r)   # subnormal elements, nonzero codes
+    r = np.full(32, big, np.float32); r[1] = -big; rows.append(r)                   # near FLT_MAX
+    rows.append(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0] * 4, np.float32))   # ties, e = 0
+    rows.append(-np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0] * 4, np.float32))
+    r = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 4.0] * 4, np.float32) * np.float32(2.0 ** -60); rows.append(r)
+    r = np.linspace(-7.99, 7.99, 32).astype(np.float32); rows.append(r)                # saturation band
+    r = np.zeros(32, np.float32); r[17] = -1e-30; rows.append(r)                       # single tiny value
+    r = np.full(32, 4.0, np.float32); rows.append(r)                                   # power-of-two amax
+    r = np.full(32, np.nextafter(np.float32(4.0), np.float32(0)), np.float32); rows.append(r)
+    r = np.full(32, np.nextafter(np.float32(8.0), np.float32(0)), np.float32); rows.append(r)
+    x = np.stack(rows)
+    return np.concatenate([x, x[::-1] * np.float32(0.5)], axis=1)   # 64 columns: two blocks per row
+
+
+def test_edge_blocks_f32():
+    check(edge_blocks(), False, None, "edge f32")
+    check(edge_blocks(1.0e37), False, "h32", "edge f32 h32")
+
+
+def test_edge_blocks_kron():
+    check(edge_blocks(1.0e36), False, rand_kron(4, 8, 3), "edge kron")
+
+
+def test_edge_blocks_bf16():
+    check(workloads.bf16_bits(edge_blocks()), True, None, "edge bf16")
+    check(workloads.bf16_bits(edge_blocks(1.0e37)), True, "h32", "edge bf16 h32")
+
+
+def test_exhaustive_bf16_values():
+    # every finite bf16 bit pattern appears, in blocks whose amax is fixed by
+    # one large element so that codes cover the whole grid at many scales
+    h = np.arange(0, 0x10000, dtype=np.uint32)
+    h = h[((h >> 7) & 0xFF) != 0xFF].astype(np.uint16)      # drop Inf/NaN
+    n = (h.size + 30) // 31 * 31
+    h = np.concatenate([h, np.zeros(n - h.size, np.uint16)]).reshape(-1, 31)
+    x = np.concatenate([h, np.full((h.shape[0], 1), 0x4100, np.uint16)], axis=1)   # 8.0
+    check(np.ascontiguousarray(x), True, None, "all bf16")
+    # rotated blocks must stay finite (sums of 32 values): below 2^120 only
+    small = h[((h.astype(np.uint32) >> 7) & 0xFF).max(axis=1) < 127 + 120]
+    xs = np.concatenate([small, np.full((small.shape[0], 1), 0x4100, np.uint16)], axis=1)
+    check(np.ascontiguousarray(xs), True, "h32", "all bf16 below 2^120, h32")
+
+
+def test_strided_input_rows():
+    rng = np.random.default_rng(5)
+    full = workloads.bf16_bits(workloads.random_blocks(rng, 40, 512))
+    x = dev_x(full, True)[:, :256]                   # ld_x = 512 > k = 256
+    announce("quantize strided", x.shape, x.stride())
+    c, s = mx.quantize_rotate(x, "h32")
+    ref = oracle.quantize(np.ascontiguousarray(full[:, :256]), rot="h32", bf16=True)
+    assert_same((c.cpu().numpy(), s.cpu().numpy()), ref, "strided")
+
+
+def test_zero_rows_is_noop():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    c, s = mx.quantize_rotate(x)
+    assert c.shape == (0, 32) and s.shape == (0, 2)
+
+
+def test_errors_raise():
+    x = torch.zeros((4, 48), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(mx.Mxfp4Error):
+        mx.quantize_rotate(x)
+
+# Full-size workloads (both operands, every code and scale byte) are checked
+# in test_gpu_gemm.test_full_workload_linear, in the benchmark's launch setup.
