@@ -1,0 +1,283 @@
+"""Benchmark of the W4A4 MXFP4 linear layer on one MI355X.
+
+One step is the whole hot path over one batch: online quantization of the
+activations (with the workload's block rotation) followed by the MXFP4 GEMM
+against pre-quantized weights (weight quantization is offline and untimed).
+Inputs are seeded synthetic tensors of the workload's shape, resident in HBM
+before the timed region; the step cycles through enough buffer sets (X, W,
+codes, scales, Y) that the working set exceeds the 256 MB Infinity Cache.
+
+Prints one JSON line:
+  value       2*M*N*K / (time of one quantize + GEMM step), TFLOP/s
+  roofline    the GEMM kernel (the dominant kernel): algorithmic FLOPs per
+              launch / its mean launch time from HIP events recorded around
+              every launch in the timed region, against the dense MXFP4 MFMA
+              peak; `traffic` = HBM bytes per launch from rocprofv3 counters
+              (profiles/), or null if the kernel source changed since
+  quantize    the quantizer kernel: algorithmic bytes (X read, codes and
+              scales written) per launch / its mean launch time, against HBM
+  copy_gbps   a plain device copy in the same run (practical HBM ceiling)
+  cpu_baseline  the CPU oracle on a bounded row sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+import workloads
+
+METRIC = "MXFP4 GEMM TFLOPS @ M=3584,K=3072,N=12288 (% peak); quantize GB/s (% HBM)"
+PEAK_MXFP4_TFLOPS = 10100.0     # MI355X dense FP4/FP6 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+CACHE_BUST_BYTES = 600 << 20    # working set per cycle of buffer sets (> 256 MB)
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "mxfp4_w4a4_quantized_amd", "csrc")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+    in profiles/<kernel>_<workload>_traffic.md, if they were taken on the
+    current kernel source (same digest); else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    d = re.search(r"^source_digest:\s*(\w+)", text, re.M)
+    t = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not d or not t or d.group(1) != digest:
+        return None
+    return float(t.group(1))
+
+
+# ----------------------------------------------------------------- GPU leg ---
+
+def gpu_leg(name: str, steps: int, warmup: int):
+    import torch
+    import mxfp4_w4a4_quantized_amd as mx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = workloads.make(name)
+    wl = inp["wl"]
+    m, n, k = wl.m, wl.n, wl.k
+    bf16_in = wl.x_dtype == "bf16"
+    out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+    if bf16_in:
+        x0 = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        x0 = torch.from_numpy(inp["x"]).to(dev)
+    if wl.rot == "h32":
+        rot = mx.HADAMARD32
+    elif wl.rot == "kron":
+        rot = mx.Kron.from_host(inp["a"], inp["b"], dev)
+    else:
+        rot = None
+    wc0, ws0 = mx.quantize_weight(torch.from_numpy(inp["w"]).to(dev), rot)   # offline
+    torch.cuda.synchronize()
+
+    set_bytes = (x0.numel() * x0.element_size() + m * k // 2 + m * k // 32 +
+                 wc0.numel() + ws0.numel() + m * n * (2 if out_dtype == torch.bfloat16 else 4))
+    nsets = max(2, -(-CACHE_BUST_BYTES // set_bytes))
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(
+            x=x0.clone(), wc=wc0.clone(), ws=ws0.clone(),
+            xc=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+            xs=torch.empty((m, k // 32), dtype=torch.uint8, device=dev),
+            y=torch.empty((m, n), dtype=out_dtype, device=dev)))
+    del x0, wc0, ws0
+    torch.cuda.synchronize()
+    log(f"workload {name}: M={m} N={n} K={k} rot={wl.rot} x={wl.x_dtype} y={wl.out_dtype}; "
+        f"{nsets} buffer sets of {set_bytes / 2**20:.1f} MiB")
+
+    def step(s):
+        mx.quantize_rotate(s["x"], rot, s["xc"], s["xs"])
+        mx.gemm(s["xc"], s["xs"], s["wc"], s["ws"], out_dtype, s["y"])
+
+    for i in range(warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)   # the stream every launch goes to
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        s = sets[i % nsets]
+        e = ev[i]
+        e[0].record(stream)
+        mx.quantize_rotate(s["x"], rot, s["xc"], s["xs"])
+        e[1].record(stream)
+        mx.gemm(s["xc"], s["xs"], s["wc"], s["ws"], out_dtype, s["y"])
+        e[2].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    q_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    g_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+
+    # plain device copy of 1 GiB: the practical HBM ceiling in this run
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    reps = 10
+    c0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nb * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    props = torch.cuda.get_device_properties(dev)
+    return dict(m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms,
+                copy_gbps=copy_gbps, nsets=nsets, device=props.name,
+                cus=props.multi_processor_count, arch=getattr(props, "gcnArchName", ""))
+
+
+# ----------------------------------------------------------------- CPU leg ---
+
+def cpu_leg(name: str, rows: int):
+    """The oracle, as it stands, on the first `rows` rows of X: quantize them
+    (with the workload's rotation) and compute their GEMM against the full
+    weight matrix (the oracle dequantizes both operands and multiplies in
+    binary64).  Weight quantization is offline on both sides and untimed."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    inp = workloads.make(name)
+    wl = inp["wl"]
+    rows = min(rows, wl.m)
+    if wl.rot == "h32":
+        xrot = wrot = "h32"
+    elif wl.rot == "kron":
+        xrot = ("kron", inp["a"], inp["b"])
+        wrot = ("kron", oracle.inverse_transpose(inp["a"]), oracle.inverse_transpose(inp["b"]))
+    else:
+        xrot = wrot = None
+    wc, ws = oracle.quantize(inp["w"], rot=wrot)
+    xs_in = np.ascontiguousarray(inp["x"][:rows])
+    t = time.perf_counter()
+    xc, xs = oracle.quantize(xs_in, rot=xrot, bf16=wl.x_dtype == "bf16")
+    y = oracle.gemm(xc, xs, wc, ws)
+    dt = time.perf_counter() - t
+    assert y.shape == (rows, wl.n)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    flops = 2.0 * rows * wl.n * wl.k
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=(f"{rows} of {wl.m} rows of X: quantize (single-threaded C) + GEMM "
+                        f"against all {wl.n} weight rows (dequantize in single-threaded C, "
+                        f"binary64 matmul on {threads} BLAS threads); {dt:.2f} s; host has "
+                        f"{os.cpu_count()} logical CPUs"),
+                seconds=dt)
+
+
+# -------------------------------------------------------------------- main ---
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="flux_up", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=-1,
+                    help="rows of X in the oracle's CPU sample (-1: all rows; 0 skips the CPU leg)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+
+    g = gpu_leg(args.workload, args.steps, args.warmup)
+    m, n, k, wl = g["m"], g["n"], g["k"], g["wl"]
+    flops = 2.0 * m * n * k
+    ms_step = g["total_ms"] / args.steps
+    g_us = float(np.mean(g["g_ms"])) * 1e3
+    q_us = float(np.mean(g["q_ms"])) * 1e3
+    g_tflops = flops / (g_us * 1e-6) / 1e12
+    x_bytes = m * k * (2 if wl.x_dtype == "bf16" else 4)
+    q_bytes = x_bytes + m * k // 2 + m * k // 32
+    q_gbps = q_bytes / (q_us * 1e-6) / 1e9
+    y_bytes = m * n * (2 if wl.out_dtype == "bf16" else 4)
+    g_bytes = (m + n) * (k // 2 + k // 32) + y_bytes
+    traffic = recorded_traffic("gemm", args.workload, source_digest("gemm.hip", "internal.h"))
+    q_traffic = recorded_traffic("quantize", args.workload, source_digest("quantize.hip", "internal.h"))
+
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "m": m, "n": n, "k": k, "x_dtype": wl.x_dtype,
+                   "rotation": wl.rot or "none", "out_dtype": wl.out_dtype,
+                   "buffer_sets": g["nsets"], "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_MXFP4_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_MXFP4_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "gemm", "us_per_launch": round(g_us, 2),
+                     "us_min": round(float(np.min(g["g_ms"])) * 1e3, 2),
+                     "algorithmic_bytes": g_bytes},
+        "quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": q_traffic, "us_per_launch": round(q_us, 2),
+                     "us_min": round(float(np.min(g["q_ms"])) * 1e3, 2),
+                     "algorithmic_bytes": q_bytes},
+        "copy_gbps": round(g["copy_gbps"], 1),
+        "device": {"name": g["device"], "arch": g["arch"], "cus": g["cus"]},
+    }
+    if args.cpu_rows != 0:
+        rows = m if args.cpu_rows < 0 else args.cpu_rows
+        log(f"CPU oracle on {rows} rows ...")
+        cb = cpu_leg(args.workload, rows)
+        cb.pop("seconds")
+        cb["value"] = round(cb["value"], 6)
+        out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
