@@ -1,0 +1,390 @@
+// Large-tile MXFP4 x MXFP4 GEMM for gfx950 on v_mfma_scale_f32_32x32x64_f8f6f4
+// (both operands E2M1: cbsz = blgp = 4).
+//
+// Y[m][n] = sum_k a_hat[m][k] * b_hat[n][k], A (activations) and B (weights)
+// K-major packed E2M1 with one E8M0 byte per 32-element block, read directly
+// by the MFMA (no dequantize pass; "AMD Quark delivers MXFP4 quantization for
+// FLUX.1-dev on Instinct MI350 with 1.92x speedup", sections "MXFP4
+// quantization for diffusion models" and "What is MXFP4 and why does it
+// eliminate dequantization overhead?").  fp32 accumulation, fp32 or bf16
+// output.
+//
+// MFMA operand layout with FP4 operands (checked on the device): lane l
+// supplies row l % 32 of its operand and the 32 K elements of block l / 32 as
+// 16 packed bytes (low nibble first) -- 16 consecutive bytes of a K-major
+// packed row -- plus one E8M0 byte for that block, picked by op_sel from a
+// 32-bit register.  Accumulator register r of lane l holds
+// D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
+//
+// Design (one workgroup of 4 waves per CU, persistent over output tiles):
+//  * Output tile 256 (N, weight rows) x 256 (M, activation rows); each wave
+//    owns a 128 x 128 quadrant as 4 x 4 MFMA fragments (256 fp32
+//    accumulators per lane).  The weight tile is the MFMA's first operand,
+//    so each lane ends with runs of 4 consecutive output columns of one row.
+//  * K advances in stages of 128 elements: per row 64 code bytes and one
+//    32-bit word of 4 scale bytes.  Stages go global -> LDS with direct LDS
+//    loads (global_load_lds_dwordx4 for codes, _dword for scales) into a ring
+//    of NBUF buffers, NBUF - 1 stages ahead of the MFMAs, with one barrier
+//    per stage.  The ring runs across tile boundaries, so the next tile's
+//    first stages load during the current tile's last MFMAs and epilogue.
+//  * A stage feeds two MFMA sub-steps; lane group g = l / 32 takes blocks
+//    2g and 2g + 1 of the stage (sub-steps s = 0, 1), so its scale register
+//    is the row's scale word shifted right by 16 g and op_sel = s.  Both
+//    operands use the same block assignment, so every product pairs the
+//    right blocks.
+//  * 16-byte chunks of a 64-byte LDS row are XOR-swizzled by
+//    ((row >> 1) ^ (row >> 2)) & 3, so every 16-lane phase of a fragment's
+//    ds_read_b128 hits 16 distinct 16-byte bank groups of the 64-bank LDS.
+//  * Fragments are double-buffered in registers: the second sub-step's
+//    fragments load while the first sub-step's MFMAs run, and the barrier
+//    sits between the two sub-steps, so the next stage's first fragments load
+//    while the second sub-step's MFMAs run.
+//  * Tiles are ordered in groups of 4 M-tiles (N fastest within a group),
+//    and workgroup b, which the dispatcher places on XCD b % 8, takes logical
+//    tiles so that the 32 workgroups of one XCD work on one compact 4 x 8
+//    block of tiles at a time and share its operand panels in that XCD's L2.
+//  * Rows beyond M or N are clamped to a valid row (never stored).  K must be
+//    a multiple of 128 (the host routes other shapes to the general kernel).
+#include "internal.h"
+
+namespace mxfp4 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BN = 256;                      // weight rows per tile
+constexpr int BM = 256;                      // activation rows per tile
+constexpr int KS = 128;                      // K elements per stage
+constexpr int RB = KS / 2;                   // code bytes per row per stage
+constexpr int ROWS = BN + BM;                // rows per stage: W then X
+constexpr int NBUF = 4;                      // LDS ring depth
+constexpr int NT = 256;                      // 4 waves
+constexpr int CODE_BYTES = ROWS * RB;        // 32 KiB
+constexpr int STAGE_BYTES = CODE_BYTES + ROWS * 4;
+constexpr int CODE_LOADS = CODE_BYTES / 1024 / 4;   // per wave, 16 B per lane
+constexpr int SCALE_LOADS = ROWS * 4 / 256 / 4;     // per wave, 4 B per lane
+constexpr int LOADS_PER_STAGE = CODE_LOADS + SCALE_LOADS;
+constexpr int GROUP_M = 4;
+
+static_assert(NBUF * STAGE_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
+
+// Chunk swizzle: rows r and r + 4, r + 8, r + 12 (one 16-lane phase of a
+// ds_read_b128 on the 64-bank LDS) and rows r, r + 2, r + 4, r + 6 (one
+// 8-lane phase of a 32-bank LDS) all land in distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+template <int S>
+__device__ __forceinline__ v16f mma(const u32x4& a, const u32x4& b, const v16f& c, uint32_t sa,
+                                    uint32_t sb) {
+  const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const v8i bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, S, (int)sa, S, (int)sb);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (low half = a), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+__device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = GROUP_M * tiles_n;
+  const int grp = L / per_group;
+  const int first_m = grp * GROUP_M;
+  const int gm = min(GROUP_M, tiles_m - first_m);
+  const int r = L - grp * per_group;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+// Wait until at most `pending` stages of this wave's direct LDS loads are
+// still in flight (vector memory loads of one wave complete in order, so a
+// count that only covers the later stages' loads is enough even with stores
+// outstanding).
+template <int PENDING>
+__device__ __forceinline__ void wait_stages() {
+  // s_waitcnt simm16 on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  constexpr int n = PENDING * LOADS_PER_STAGE;
+  static_assert(n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles_m, int tiles_n,
+                                                           int grid, int xcd_remap, int y_vec) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE_BYTES];
+
+  const int ntiles = tiles_m * tiles_n;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.x;
+  const int slot = xcd_remap ? (b & 7) * (grid >> 3) + (b >> 3) : b;
+  if (slot >= ntiles) return;
+  const int nk = g.k / KS;
+  const int total = ((ntiles - slot + grid - 1) / grid) * nk;
+  const uint32_t kbytes = (uint32_t)g.k / 2, kblocks = (uint32_t)g.k / 32;
+
+  // ---- direct LDS load plan: waves 0, 1 load weight rows, waves 2, 3 activation rows
+  const bool w_side = wave < 2;
+  const uint8_t* cbase = w_side ? g.b_codes : g.a_codes;
+  const uint8_t* sbase = w_side ? g.b_scales : g.a_scales;
+  const int lim = (w_side ? g.n : g.m) - 1;
+  const int half = wave & 1;
+  uint32_t coff[CODE_LOADS], soff[SCALE_LOADS];
+  auto plan = [&](int j) {   // j-th tile of this workgroup
+    int tm, tn;
+    tile_coords(j * grid + slot, tiles_m, tiles_n, tm, tn);
+    const int r0 = w_side ? tn * BN : tm * BM;
+#pragma unroll
+    for (int i = 0; i < CODE_LOADS; ++i) {
+      const int row = 16 * (CODE_LOADS * half + i) + (lane >> 2);   // row within this side
+      const uint32_t grow = (uint32_t)min(r0 + row, lim);
+      coff[i] = grow * kbytes + 16u * (uint32_t)((lane & 3) ^ swz(row));
+    }
+#pragma unroll
+    for (int i = 0; i < SCALE_LOADS; ++i) {
+      const int row = 64 * (SCALE_LOADS * half + i) + lane;
+      soff[i] = (uint32_t)min(r0 + row, lim) * kblocks;
+    }
+  };
+  // Issue state: tile ij of this workgroup, stage ikt within it, ring slot
+  // ibuf.  The loads of one stage are issued in pieces spread through the
+  // MFMA stream (issue_codes / issue_scales), so that the four waves never
+  // stall together on the texture unit; advance() then moves to the next
+  // stage.
+  int ij = 0, ikt = 0, ibuf = 0;
+  plan(0);
+  auto issue_codes = [&](int i0, int i1) {
+    uint8_t* dst = lds + ibuf * STAGE_BYTES;
+    const uint8_t* cb = cbase + ikt * RB;
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+      __builtin_amdgcn_global_load_lds(cb + coff[i], dst + (CODE_LOADS * wave + i) * 1024, 16, 0, 0);
+  };
+  auto issue_scales = [&]() {
+    uint8_t* dst = lds + ibuf * STAGE_BYTES;
+    const uint8_t* sb = sbase + ikt * 4;
+#pragma unroll
+    for (int i = 0; i < SCALE_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds(sb + soff[i],
+                                       dst + CODE_BYTES + (64 * (SCALE_LOADS * wave + i)) * 4, 4, 0, 0);
+  };
+  auto advance = [&]() {
+    ibuf = ibuf + 1 == NBUF ? 0 : ibuf + 1;
+    if (++ikt == nk) {
+      ikt = 0;
+      if ((++ij) * nk < total) plan(ij);
+    }
+  };
+
+  const int wn = wave & 1, wm = wave >> 1;
+  const int lr = lane & 31, lg = lane >> 5;
+  // LDS byte offsets of this lane's fragment rows (stage-relative)
+  int wrow[4], xrow[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    wrow[f] = wn * 128 + 32 * f + lr;
+    xrow[f] = BN + wm * 128 + 32 * f + lr;
+  }
+  // Lane group g takes blocks 2g, 2g + 1 of a stage: a 16-bit load of the
+  // row's scale bytes 2g, 2g + 1 leaves the sub-step s byte at op_sel = s.
+  auto load_scales = [&](const uint8_t* sbuf, uint32_t (&sw)[4], uint32_t (&sx)[4]) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      sw[f] = *reinterpret_cast<const uint16_t*>(sbuf + CODE_BYTES + 4 * wrow[f] + 2 * lg);
+      sx[f] = *reinterpret_cast<const uint16_t*>(sbuf + CODE_BYTES + 4 * xrow[f] + 2 * lg);
+    }
+  };
+  auto load_frags = [&](const uint8_t* sbuf, int s, u32x4 (&wf)[4], u32x4 (&xf)[4]) {
+    const int c = 2 * lg + s;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      wf[f] = *reinterpret_cast<const u32x4*>(sbuf + wrow[f] * RB + 16 * (c ^ swz(wrow[f])));
+      xf[f] = *reinterpret_cast<const u32x4*>(sbuf + xrow[f] * RB + 16 * (c ^ swz(xrow[f])));
+    }
+  };
+
+  // The ring always has NBUF - 1 stages in flight: one stage is issued per
+  // computed stage, past the end too (those re-read rows of the last tile into
+  // a free slot and are never used), so every wait count is a constant.
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p) {
+    if (p > 0) advance();
+    issue_codes(0, CODE_LOADS);
+    issue_scales();
+  }
+
+  // stage 0: wait for it, then load its scales and first fragments
+  wait_stages<NBUF - 2>();
+  __builtin_amdgcn_s_barrier();
+  uint32_t sw[4], sx[4];
+  u32x4 wa[4], xa[4];
+  load_scales(lds, sw, sx);
+  load_frags(lds, 0, wa, xa);
+
+  int cbuf = 0;   // ring slot of the stage being computed
+  for (int j = 0; j * nk < total; ++j) {
+    v16f acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
+
+    for (int kt = 0; kt < nk; ++kt) {
+      // Stage it + 1 is loaded once this wave's loads of it are done and every
+      // wave has passed the barrier.  The barrier also guarantees that all
+      // waves have finished reading stage it - 1, whose slot this iteration's
+      // loads overwrite.  No fence: a release fence on LDS would also wait for
+      // the loads still in flight.
+      advance();   // to stage it + NBUF - 1 (its branch stays out of the MFMA block)
+      wait_stages<NBUF - 3>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+
+      const uint8_t* sbuf = lds + cbuf * STAGE_BYTES;
+      cbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;
+      const uint8_t* nbuf = lds + cbuf * STAGE_BYTES;
+
+      // sub-step 0 MFMAs, interleaved with the sub-step 1 reads and half of
+      // the loads of stage it + NBUF - 1
+      u32x4 wb[4], xb[4];
+      load_frags(sbuf, 1, wb, xb);
+      issue_codes(0, 4);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) acc[a][bb] = mma<0>(wa[a], xa[bb], acc[a][bb], sw[a], sx[bb]);
+      // one MFMA first (its wait then covers only older reads), the reads
+      // early (they feed sub-step 1), then the loads between MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // 1 global load
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // 3 MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);     // 1 global load
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // 2 MFMA
+
+      // sub-step 1 MFMAs, interleaved with the next stage's scale and
+      // sub-step 0 reads (after the last stage these read a slot that is
+      // never used) and the other half of the loads
+      uint32_t sw1[4], sx1[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        sw1[f] = sw[f];
+        sx1[f] = sx[f];
+      }
+      load_scales(nbuf, sw, sx);
+      load_frags(nbuf, 0, wa, xa);
+      issue_codes(4, CODE_LOADS);
+      issue_scales();
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) acc[a][bb] = mma<1>(wb[a], xb[bb], acc[a][bb], sw1[a], sx1[bb]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      }
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // 1 global load
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // last MFMA
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- epilogue of this workgroup's j-th tile
+    int tm, tn;
+    tile_coords(j * grid + slot, tiles_m, tiles_n, tm, tn);
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int m = tm * BM + wm * 128 + 32 * bb + lr;
+      if (m >= g.m) continue;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int n = tn * BN + wn * 128 + 32 * a + 8 * t + 4 * lg;
+          const float v0 = acc[a][bb][4 * t], v1 = acc[a][bb][4 * t + 1];
+          const float v2 = acc[a][bb][4 * t + 2], v3 = acc[a][bb][4 * t + 3];
+          if constexpr (BF16OUT) {
+            uint16_t* yp = static_cast<uint16_t*>(g.y) + (int64_t)m * g.ld_y + n;
+            const uint32_t lo = pack_bf16(v0, v1), hi = pack_bf16(v2, v3);
+            if (y_vec && n + 3 < g.n) {
+              *reinterpret_cast<uint2*>(yp) = make_uint2(lo, hi);
+            } else {
+              if (n < g.n) yp[0] = (uint16_t)lo;
+              if (n + 1 < g.n) yp[1] = (uint16_t)(lo >> 16);
+              if (n + 2 < g.n) yp[2] = (uint16_t)hi;
+              if (n + 3 < g.n) yp[3] = (uint16_t)(hi >> 16);
+            }
+          } else {
+            float* yp = static_cast<float*>(g.y) + (int64_t)m * g.ld_y + n;
+            if (y_vec && n + 3 < g.n) {
+              *reinterpret_cast<float4*>(yp) = make_float4(v0, v1, v2, v3);
+            } else {
+              if (n < g.n) yp[0] = v0;
+              if (n + 1 < g.n) yp[1] = v1;
+              if (n + 2 < g.n) yp[2] = v2;
+              if (n + 3 < g.n) yp[3] = v3;
+            }
+          }
+        }
+      }
+    }
+  }
+  // no direct LDS load may still be writing when the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace
+
+bool gemm_large_supported(const GemmArgs& g) {
+  return (g.k % KS) == 0 && ((uintptr_t)g.a_scales % 4) == 0 && ((uintptr_t)g.b_scales % 4) == 0 &&
+         (int64_t)g.m * (g.k / 2) < (int64_t(1) << 32) && (int64_t)g.n * (g.k / 2) < (int64_t(1) << 32);
+}
+
+hipError_t launch_gemm_large(const GemmArgs& g, hipStream_t s) {
+  const int tiles_m = (g.m + BM - 1) / BM, tiles_n = (g.n + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  int grid = cu_count();
+  if (ntiles < grid) grid = ntiles;
+  const int xcd_remap = (grid % 8) == 0;
+  const size_t ybytes = g.y_bf16 ? 2 : 4;
+  const int y_vec = (((uintptr_t)g.y) % (4 * ybytes) == 0) && (g.ld_y % 4 == 0);
+  if (g.y_bf16)
+    gemm_large_kernel<true><<<grid, NT, 0, s>>>(g, tiles_m, tiles_n, grid, xcd_remap, y_vec);
+  else
+    gemm_large_kernel<false><<<grid, NT, 0, s>>>(g, tiles_m, tiles_n, grid, xcd_remap, y_vec);
+  return hipGetLastError();
+}
+
+}  // namespace mxfp4

@@ -34,4 +34,9 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
+// Large-tile persistent kernel (gemm_large.hip): K a multiple of 128,
+// 4-byte aligned scale pointers, operand code bytes below 4 GiB.
+bool gemm_large_supported(const GemmArgs& a);
+hipError_t launch_gemm_large(const GemmArgs& a, hipStream_t s);
+
 }  // namespace mxfp4

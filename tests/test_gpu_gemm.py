@@ -91,6 +91,43 @@ def test_random_operands(m, n, k):
     check_full(ac, as_, bc, bs, "random")
 
 
+# Shapes for the large-tile persistent kernel (K a multiple of 128, M > 64):
+# one K stage, fewer stages than the load ring, ragged M and N, fewer tiles
+# than CUs (grid not a multiple of 8), and more tiles than CUs (several tiles
+# per workgroup, the load ring running across tile boundaries).
+LARGE_SHAPES = [
+    (256, 256, 128), (257, 300, 256), (520, 1030, 384), (96, 2048, 512),
+    (700, 100, 640), (1024, 768, 1024), (4352, 4352, 128), (2304, 4608, 384),
+]
+
+
+@pytest.mark.parametrize("m,n,k", LARGE_SHAPES)
+def test_large_tile_shapes(m, n, k):
+    rng = np.random.default_rng(m * 31 + n * 17 + k)
+    ac, as_ = workloads.random_mxfp4(rng, m, k)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+    check_full(ac, as_, bc, bs, "large-tile")
+
+
+def test_large_tile_strided_output():
+    rng = np.random.default_rng(80)
+    m, n, k = 300, 520, 256
+    ac, as_ = workloads.random_mxfp4(rng, m, k)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+    for dt, fill in ((torch.float32, 7.0), (torch.bfloat16, 3.0)):
+        big = torch.full((m, n + 12), fill, dtype=dt, device=DEV)
+        y = big[:, 4:4 + n]                                          # ld_y = n + 12, offset 4
+        announce("gemm large strided", m, n, k, dt)
+        mx.gemm(*map(to_dev, (ac, as_, bc, bs)), dt, y=y)
+        torch.cuda.synchronize()
+        ref = oracle.gemm(ac, as_, bc, bs)
+        if dt == torch.float32:
+            err = norm_err(y.cpu().numpy(), ref, row_norms(ac, as_), row_norms(bc, bs))
+            assert err <= TOL
+        host = big.float().cpu().numpy()
+        assert (host[:, :4] == fill).all() and (host[:, 4 + n:] == fill).all()   # no stray writes
+
+
 def test_extreme_scales():
     # scale bytes near both ends of the E8M0 range (products stay finite)
     rng = np.random.default_rng(77)
