@@ -1,14 +1,18 @@
 // Online MXFP4 activation quantizer for gfx950 (CDNA4).
 //
-// One thread owns one 32-element block: it loads the block with four 16-byte
-// loads (bf16) or eight (fp32), widens to fp32, applies the optional block
-// rotation entirely in registers, reduces the block amax, derives the E8M0
-// scale from the amax exponent bits, converts pairs of scaled values with the
-// hardware E2M1 converter (v_cvt_scalef32_pk_fp4_f32, round-to-nearest-even,
-// saturating, sign kept on zero) and writes its 16 code bytes with one
-// 16-byte store and its scale with one byte store.  Consecutive threads own
-// consecutive blocks, so every wave writes 1 KiB of codes and 64 scale bytes
-// contiguously.
+// Each lane owns one 32-element block.  A wave first loads its 64 blocks with
+// contiguous 1 KiB loads (lane l reads 16-byte chunk l of each KiB, so every
+// load instruction is fully coalesced), parks them in a wave-private LDS
+// slab, and then each lane reads back its own block.  In the slab, chunk q of
+// block i sits at chunk position q ^ f(i) of the block's row, so both the
+// coalesced writes and the per-block reads hit distinct banks.  The lane then
+// widens to fp32, applies the optional block rotation entirely in registers,
+// reduces the block amax, derives the E8M0 scale from the amax exponent bits,
+// converts pairs of values with the hardware E2M1 converter, whose scale
+// operand is the block scale (v_cvt_scalef32_pk_fp4_f32: divide by the
+// power-of-two scale, round to nearest even, saturate, keep the sign on zero) and writes its 16 code bytes with one 16-byte store (consecutive
+// lanes, consecutive blocks) and its scale with one byte store.  X is read
+// once, with non-temporal loads.
 //
 // Method (page titles and sections as the pages give them):
 //  - block format: "AMD Quark delivers MXFP4 quantization for FLUX.1-dev on
@@ -90,39 +94,75 @@ __device__ __forceinline__ void kron32(const float* __restrict__ fa, const float
   }
 }
 
+// Chunk swizzle inside the LDS slab: a block is CPB 16-byte chunks; the
+// 16 lanes of one ds_read_b128 phase read chunk q of 16 consecutive blocks,
+// which land in 16 distinct 16-byte bank groups of the 64-bank LDS.
+template <int CPB>
+__device__ __forceinline__ int slab_swz(int blk) {
+  return CPB == 4 ? (blk >> 2) & 3 : (blk >> 1) & 7;
+}
+
 // rot: 0 none, 1 Hadamard-32, 2 Kronecker (P x Q)
 template <bool BF16, int ROT, int P, int Q>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int dense) {
+  constexpr int CPB = BF16 ? 4 : 8;   // 16-byte chunks per 32-element block
+  __shared__ u32x4 slab[kThreads / 64][64 * CPB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t nblk = a.rows * a.nblk_row;
+  const uint32_t wb0 = (blockIdx.x * (kThreads / 64) + wave) * 64;   // first block of this wave
+  if (wb0 >= nblk) return;
+  const int esz = BF16 ? 2 : 4;
+  const uint8_t* x = static_cast<const uint8_t*>(a.x);
+
+  // coalesced loads: instruction u covers chunks 64u .. 64u + 63 of the wave
+  u32x4 ld[CPB];
+#pragma unroll
+  for (int u = 0; u < CPB; ++u) {
+    const int c = 64 * u + lane;
+    const uint32_t blk = wb0 + c / CPB;
+    const int q = c % CPB;
+    if (blk < nblk) {
+      int64_t off;
+      if (dense) {
+        off = (int64_t)blk * 32 * esz;
+      } else {
+        const uint32_t r = blk / a.nblk_row;
+        off = ((int64_t)r * a.ld_x + (int64_t)(blk - r * a.nblk_row) * 32) * esz;
+      }
+      ld[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off + 16 * q));
+    } else {
+      ld[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < CPB; ++u) {
+    const int c = 64 * u + lane;
+    const int bl = c / CPB;
+    slab[wave][bl * CPB + ((c % CPB) ^ slab_swz<CPB>(bl))] = ld[u];
+  }
+  // The slab is private to this wave and LDS operations of one wave complete
+  // in order, so the reads below see the writes above without a barrier.
+  const uint32_t gid = wb0 + lane;
   if (gid >= nblk) return;
-  const uint32_t r = gid / a.nblk_row;
-  const uint32_t b = gid - r * a.nblk_row;
+  u32x4 q4[CPB];
+#pragma unroll
+  for (int q = 0; q < CPB; ++q) q4[q] = slab[wave][lane * CPB + (q ^ slab_swz<CPB>(lane))];
 
   float v[32];
   if constexpr (BF16) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(a.x) + (int64_t)r * a.ld_x + (int64_t)b * 32);
-    u32x4 q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = __builtin_nontemporal_load(src + i);   // X is read once
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t w[4] = {q[i][0], q[i][1], q[i][2], q[i][3]};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = bf16_lo(w[j]);
-        v[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+        v[8 * i + 2 * j] = bf16_lo(q4[i][j]);
+        v[8 * i + 2 * j + 1] = bf16_hi(q4[i][j]);
       }
     }
   } else {
-    const f32x4* src = reinterpret_cast<const f32x4*>(
-        static_cast<const float*>(a.x) + (int64_t)r * a.ld_x + (int64_t)b * 32);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x4 f = __builtin_nontemporal_load(src + i);
-      v[4 * i] = f[0]; v[4 * i + 1] = f[1]; v[4 * i + 2] = f[2]; v[4 * i + 3] = f[3];
-    }
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * i + j] = __uint_as_float(q4[i][j]);
   }
 
   if constexpr (ROT == 1) hadamard32(v);
@@ -137,17 +177,20 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   // of amax minus 2 (subnormal and zero amax have field 0 and clamp).
   const uint32_t ef = __float_as_uint(amax) >> 23;
   const uint32_t sbyte = ef > 2u ? ef - 2u : 0u;
-  // 2^-e as an fp32 with exponent field 254 - sbyte (always normal)
-  const float inv = __uint_as_float((254u - sbyte) << 23);
+  // The block scale 2^e as fp32 (2^-127 is the subnormal 0x00400000).  The
+  // converter divides by its scale operand exactly -- it equals converting
+  // v * 2^-e with scale 1 for every finite input, checked on the device for
+  // all bf16 values and e in [-127, 125] -- so no separate multiply is needed.
+  const float scale = __uint_as_float(sbyte ? sbyte << 23 : 0x00400000u);
 
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t acc = 0;
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 0] * inv, v[8 * i + 1] * inv, 1.0f, 0);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 2] * inv, v[8 * i + 3] * inv, 1.0f, 1);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 4] * inv, v[8 * i + 5] * inv, 1.0f, 2);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 6] * inv, v[8 * i + 7] * inv, 1.0f, 3);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 0], v[8 * i + 1], scale, 0);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 2], v[8 * i + 3], scale, 1);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 4], v[8 * i + 5], scale, 2);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 6], v[8 * i + 7], scale, 3);
     w[i] = acc;
   }
   uint4* dst = reinterpret_cast<uint4*>(a.codes) + gid;
@@ -159,18 +202,19 @@ template <bool BF16>
 hipError_t dispatch(const QuantArgs& a, hipStream_t s) {
   const uint32_t nblk = a.rows * a.nblk_row;
   const dim3 grid((nblk + kThreads - 1) / kThreads), block(kThreads);
+  const int dense = a.ld_x == (int64_t)a.nblk_row * 32;
   if (a.rot == 0) {
-    quantize_kernel<BF16, 0, 1, 32><<<grid, block, 0, s>>>(a);
+    quantize_kernel<BF16, 0, 1, 32><<<grid, block, 0, s>>>(a, dense);
   } else if (a.rot == 1) {
-    quantize_kernel<BF16, 1, 1, 32><<<grid, block, 0, s>>>(a);
+    quantize_kernel<BF16, 1, 1, 32><<<grid, block, 0, s>>>(a, dense);
   } else {
     switch (a.p) {
-      case 1: quantize_kernel<BF16, 2, 1, 32><<<grid, block, 0, s>>>(a); break;
-      case 2: quantize_kernel<BF16, 2, 2, 16><<<grid, block, 0, s>>>(a); break;
-      case 4: quantize_kernel<BF16, 2, 4, 8><<<grid, block, 0, s>>>(a); break;
-      case 8: quantize_kernel<BF16, 2, 8, 4><<<grid, block, 0, s>>>(a); break;
-      case 16: quantize_kernel<BF16, 2, 16, 2><<<grid, block, 0, s>>>(a); break;
-      case 32: quantize_kernel<BF16, 2, 32, 1><<<grid, block, 0, s>>>(a); break;
+      case 1: quantize_kernel<BF16, 2, 1, 32><<<grid, block, 0, s>>>(a, dense); break;
+      case 2: quantize_kernel<BF16, 2, 2, 16><<<grid, block, 0, s>>>(a, dense); break;
+      case 4: quantize_kernel<BF16, 2, 4, 8><<<grid, block, 0, s>>>(a, dense); break;
+      case 8: quantize_kernel<BF16, 2, 8, 4><<<grid, block, 0, s>>>(a, dense); break;
+      case 16: quantize_kernel<BF16, 2, 16, 2><<<grid, block, 0, s>>>(a, dense); break;
+      case 32: quantize_kernel<BF16, 2, 32, 1><<<grid, block, 0, s>>>(a, dense); break;
       default: return hipErrorInvalidValue;
     }
   }
