@@ -3,6 +3,8 @@
 One step is the whole hot path over one batch: online quantization of the
 activations (with the workload's block rotation) followed by the MXFP4 GEMM
 against pre-quantized weights (weight quantization is offline and untimed).
+Both operands use the library's GEMM-native tiled layout: the quantizer
+writes X's codes and scales tiled, and W is quantized to it offline.
 Inputs are seeded synthetic tensors of the workload's shape, resident in HBM
 before the timed region; the step cycles through enough buffer sets (X, W,
 codes, scales, Y) that the working set exceeds the 256 MB Infinity Cache.
@@ -95,18 +97,20 @@ def gpu_leg(name: str, steps: int, warmup: int):
         rot = mx.Kron.from_host(inp["a"], inp["b"], dev)
     else:
         rot = None
-    wc0, ws0 = mx.quantize_weight(torch.from_numpy(inp["w"]).to(dev), rot)   # offline
+    lay = mx.TILED
+    wc0, ws0 = mx.quantize_weight(torch.from_numpy(inp["w"]).to(dev), rot, layout=lay)   # offline
     torch.cuda.synchronize()
 
-    set_bytes = (x0.numel() * x0.element_size() + m * k // 2 + m * k // 32 +
+    mp = mx.padded_rows(m)
+    set_bytes = (x0.numel() * x0.element_size() + mp * k // 2 + mp * k // 32 +
                  wc0.numel() + ws0.numel() + m * n * (2 if out_dtype == torch.bfloat16 else 4))
     nsets = max(2, -(-CACHE_BUST_BYTES // set_bytes))
     sets = []
     for _ in range(nsets):
         sets.append(dict(
             x=x0.clone(), wc=wc0.clone(), ws=ws0.clone(),
-            xc=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
-            xs=torch.empty((m, k // 32), dtype=torch.uint8, device=dev),
+            xc=torch.empty((mp, k // 2), dtype=torch.uint8, device=dev),
+            xs=torch.empty((mp, k // 32), dtype=torch.uint8, device=dev),
             y=torch.empty((m, n), dtype=out_dtype, device=dev)))
     del x0, wc0, ws0
     torch.cuda.synchronize()
@@ -114,8 +118,8 @@ def gpu_leg(name: str, steps: int, warmup: int):
         f"{nsets} buffer sets of {set_bytes / 2**20:.1f} MiB")
 
     def step(s):
-        mx.quantize_rotate(s["x"], rot, s["xc"], s["xs"])
-        mx.gemm(s["xc"], s["xs"], s["wc"], s["ws"], out_dtype, s["y"])
+        mx.quantize_rotate(s["x"], rot, s["xc"], s["xs"], layout=lay)
+        mx.gemm(s["xc"], s["xs"], s["wc"], s["ws"], out_dtype, s["y"], layout=lay)
 
     for i in range(warmup):
         step(sets[i % nsets])
@@ -132,9 +136,9 @@ def gpu_leg(name: str, steps: int, warmup: int):
         s = sets[i % nsets]
         e = ev[i]
         e[0].record(stream)
-        mx.quantize_rotate(s["x"], rot, s["xc"], s["xs"])
+        mx.quantize_rotate(s["x"], rot, s["xc"], s["xs"], layout=lay)
         e[1].record(stream)
-        mx.gemm(s["xc"], s["xs"], s["wc"], s["ws"], out_dtype, s["y"])
+        mx.gemm(s["xc"], s["xs"], s["wc"], s["ws"], out_dtype, s["y"], layout=lay)
         e[2].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
@@ -252,7 +256,7 @@ def main():
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {"workload": args.workload, "m": m, "n": n, "k": k, "x_dtype": wl.x_dtype,
-                   "rotation": wl.rot or "none", "out_dtype": wl.out_dtype,
+                   "rotation": wl.rot or "none", "out_dtype": wl.out_dtype, "layout": "tiled",
                    "buffer_sets": g["nsets"], "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_MXFP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_MXFP4_TFLOPS, 4),

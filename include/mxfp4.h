@@ -40,12 +40,25 @@
  *  - Argument checks are synchronous and nothing is launched when they fail.
  *    No exception crosses the ABI and the library never aborts.
  *
- * Packed layouts (row-major, K contiguous -- "K-major" for both operands):
+ * Packed layouts.  Both operands of a GEMM use the same layout.
+ *  MXFP4_LAYOUT_ROWMAJOR (the interchange format; K contiguous, "K-major"):
  *  - codes [rows][K/2] uint8: element 2j of a row in the low nibble of byte j,
  *    element 2j+1 in the high nibble.  E2M1 code = sign<<3 | magnitude index
  *    into {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
  *  - scales [rows][K/32] uint8: E8M0 byte s of block b means 2^(s-127).
  *  Both are dense (row strides K/2 and K/32 bytes).
+ *  MXFP4_LAYOUT_TILED (the GEMM-native format; K a multiple of 128): rows are
+ *  grouped in tiles of 256 and K in stages of 128 elements (4 blocks).
+ *  With T = ceil(rows / 256) and S = K / 128:
+ *  - codes [T][S][256][64] bytes: in tile t, stage s, row r (global row
+ *    256 t + r), block 4 s + c (c = 0..3) occupies the 16 bytes at
+ *    r * 64 + 16 * (c ^ ((r >> 1 ^ r >> 2) & 3)), with the row-major nibble
+ *    order inside the block;
+ *  - scales [T][S][256][4] bytes: the scale of block 4 s + c of row r at r * 4 + c.
+ *  Rows rows .. 256 T - 1 are padding; the quantizer writes them as zero codes
+ *  and zero scale bytes, and the GEMM never stores their results.  Every load
+ *  the GEMM makes of a tiled operand is then a contiguous 1 KiB (codes) or
+ *  256-byte (scales) run.  mxfp4_tiled_bytes gives the buffer sizes.
  *
  * Quantizer rule (per 32-block, after the optional rotation, all in fp32):
  *  amax = max |y_i|;  e = max(floor(log2 amax) - 2, -127), e = -127 for
@@ -90,6 +103,12 @@ typedef enum {
     MXFP4_ROT_KRON = 2         /* y = (A (x) B) x, A p x p, B q x q, p*q=32 */
 } mxfp4_rot_kind;
 
+/* Memory layout of packed codes and scales (see "Packed layouts" above). */
+typedef enum {
+    MXFP4_LAYOUT_ROWMAJOR = 0,
+    MXFP4_LAYOUT_TILED = 1
+} mxfp4_layout;
+
 /* Rotation descriptor (host struct; read during the call).
  * HADAMARD32 evaluation order (fp32, no fused ops): butterflies
  *   (u, v) -> (u + v, u - v) with strides 1, 2, 4, 8, 16, then a multiply by
@@ -111,37 +130,50 @@ typedef struct {
  *   x       device, [rows][ld_x] elements of x_dtype (F32 or BF16); the first
  *           k columns of each row are quantized.  16-byte aligned, and ld_x a
  *           multiple of 8 (BF16) or 4 (F32), else MXFP4_ERR_UNSUPPORTED.
- *   rows    >= 0 (0 is a no-op);  k > 0, multiple of 32;  ld_x >= k.
+ *   rows    >= 0 (0 is a no-op);  k > 0, multiple of 32 (of 128 for TILED);
+ *           ld_x >= k.
  *   rot     NULL or kind NONE: no rotation.
- *   codes   device, [rows][k/2] bytes, 16-byte aligned (written).
- *   scales  device, [rows][k/32] bytes (written).
- * Errors: INVALID_ARG for null pointers (when rows > 0), k % 32 != 0, k <= 0,
- *   rows < 0, ld_x < k, bad dtype, bad rotation (unknown kind, p*q != 32,
- *   null factor pointers); UNSUPPORTED for misalignment or
- *   rows * k / 32 >= 2^31; HIP if the launch fails. */
+ *   layout  mxfp4_layout of the outputs.
+ *   codes   device, 16-byte aligned (written): [rows][k/2] bytes (ROWMAJOR),
+ *           or the tiled codes, padding rows included (TILED).
+ *   scales  device (written): [rows][k/32] bytes (ROWMAJOR), or the tiled
+ *           scales (TILED, 4-byte aligned).
+ * Errors: INVALID_ARG for null pointers (when rows > 0), k % 32 != 0 (k % 128
+ *   for TILED), k <= 0, rows < 0, ld_x < k, bad dtype or layout, bad rotation
+ *   (unknown kind, p*q != 32, null factor pointers); UNSUPPORTED for
+ *   misalignment or rows * k / 32 >= 2^31; HIP if the launch fails. */
 MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype,
                                              int64_t rows, int64_t k, int64_t ld_x,
-                                             const mxfp4_rotation* rot,
+                                             const mxfp4_rotation* rot, int32_t layout,
                                              uint8_t* codes, uint8_t* scales,
                                              void* stream);
 
 /* Y = A * B^T on MXFP4 operands, fp32 accumulation.
- *   a_codes/a_scales  device, A in the packed layout above, m rows.
- *   b_codes/b_scales  device, B in the packed layout above, n rows
+ *   a_codes/a_scales  device, A (m rows) in `layout`.
+ *   b_codes/b_scales  device, B (n rows) in `layout`
  *                     (for a linear layer B = W, [out_features][in_features]).
- *   m, n >= 0 (0 is a no-op), k > 0 multiple of 32.
+ *   m, n >= 0 (0 is a no-op), k > 0 multiple of 32 (of 128 for TILED).
  *   y       device, [m][ld_y] elements of y_dtype (F32 or BF16), ld_y >= n;
  *           element (i, j) = sum over blocks of 2^(sa-127) 2^(sb-127) times
  *           the block's E2M1 dot product, accumulated in fp32, rounded to
  *           bf16 (nearest-even) for BF16 output.
- *   Code pointers 16-byte aligned.
- * Errors: INVALID_ARG for null pointers (when m, n > 0), k % 32 != 0, k <= 0,
- *   negative sizes, ld_y < n, bad dtype; UNSUPPORTED for misaligned code
- *   pointers or m, n, k >= 2^30; HIP if the launch fails. */
+ *   Code pointers 16-byte aligned; TILED scale pointers 4-byte aligned.
+ * Errors: INVALID_ARG for null pointers (when m, n > 0), k % 32 != 0 (k % 128
+ *   for TILED), k <= 0, negative sizes, ld_y < n, bad dtype or layout;
+ *   UNSUPPORTED for misaligned pointers or m, n, k >= 2^30; HIP if the launch
+ *   fails. */
 MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
-                                  int64_t k, void* y, int32_t y_dtype, int64_t ld_y,
+                                  int64_t k, int32_t layout, void* y, int32_t y_dtype, int64_t ld_y,
                                   void* stream);
+
+/* Buffer sizes of a TILED operand with `rows` rows and `k` columns (k > 0, a
+ * multiple of 128; rows >= 0): *codes_bytes = 256 T * k / 2 and
+ * *scales_bytes = 256 T * k / 32 with T = ceil(rows / 256).
+ * Errors: INVALID_ARG for null pointers, rows < 0, or k not a positive
+ *   multiple of 128. */
+MXFP4_API mxfp4_status mxfp4_tiled_bytes(int64_t rows, int64_t k, int64_t* codes_bytes,
+                                         int64_t* scales_bytes);
 
 /* Host helper for the offline weight fold of a Kronecker transform: since
  * (A (x) B)^-T = A^-T (x) B^-T, quantizing the weights with KRON factors
@@ -157,7 +189,7 @@ MXFP4_API mxfp4_status mxfp4_inverse_transpose(const float* m, int32_t n, float*
 MXFP4_API const char* mxfp4_status_string(int32_t status);
 
 /* ABI version of this header (bumped on incompatible changes). */
-#define MXFP4_ABI_VERSION 1
+#define MXFP4_ABI_VERSION 2
 MXFP4_API int32_t mxfp4_abi_version(void);
 
 #ifdef __cplusplus

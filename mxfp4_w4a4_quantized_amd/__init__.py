@@ -4,14 +4,20 @@ Every step of the layer runs in the HIP library's kernels; this module only
 marshals torch tensors (device memory and the current HIP stream) into the
 C-ABI calls declared in include/mxfp4.h:
 
-  quantize_rotate(x, rot)            online MXFP4 quantization of activations,
+  quantize_rotate(x, rot, layout)    online MXFP4 quantization of activations,
                                      with an optional per-32-block rotation
-  gemm(a_codes, a_scales, b_codes, b_scales, out_dtype)
+  gemm(a_codes, a_scales, b_codes, b_scales, out_dtype, layout=...)
                                      Y = A * B^T on packed MXFP4 operands
   linear(x, w_codes, w_scales, rot)  the two above, back to back
   quantize_weight(w, rot)            offline weight quantization with the
                                      weight side of the rotation
   inverse_transpose(m)               host helper for the Kronecker weight fold
+
+Layouts: ROWMAJOR (codes [rows, k/2], scales [rows, k/32]) or TILED, the
+GEMM-native layout of include/mxfp4.h (256-row tiles x 128-element stages,
+each stage stored as the GEMM's LDS image; tensors of padded_rows(rows) rows
+holding the same bytes in tiled order).  tile_host / untile_host convert on
+the host (a pure byte permutation, for tests and offline weight prep).
 
 Rotations: None, HADAMARD32, or Kron(a, b) -- a learned Kronecker-factored
 32x32 transform A (x) B ("KroQuant: ...", abstract and "Tiefenanalyse"); the
@@ -34,10 +40,12 @@ LIB_PATH = os.path.join(_HERE, "libmxfp4.so")
 MXFP4_OK, MXFP4_ERR_INVALID_ARG, MXFP4_ERR_UNSUPPORTED, MXFP4_ERR_HIP = 0, 1, 2, 3
 MXFP4_F32, MXFP4_BF16 = 0, 1
 ROT_NONE, ROT_HADAMARD32, ROT_KRON = 0, 1, 2
+ROWMAJOR, TILED = 0, 1
+TILE_ROWS, TILE_K = 256, 128
 
 HADAMARD32 = "h32"
 
-EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_gemm", "mxfp4_inverse_transpose",
+EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_gemm", "mxfp4_tiled_bytes", "mxfp4_inverse_transpose",
             "mxfp4_status_string", "mxfp4_abi_version")
 
 
@@ -66,9 +74,11 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.mxfp4_quantize_rotate.restype = i32
-    L.mxfp4_quantize_rotate.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), vp, vp, vp]
+    L.mxfp4_quantize_rotate.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), i32, vp, vp, vp]
     L.mxfp4_gemm.restype = i32
-    L.mxfp4_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i32, i64, vp]
+    L.mxfp4_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, i32, vp, i32, i64, vp]
+    L.mxfp4_tiled_bytes.restype = i32
+    L.mxfp4_tiled_bytes.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.mxfp4_inverse_transpose.restype = i32
     L.mxfp4_inverse_transpose.argtypes = [vp, i32, vp]
     L.mxfp4_status_string.restype = ctypes.c_char_p
@@ -135,35 +145,66 @@ def _dtype_code(dt) -> int:
     raise ValueError(f"unsupported dtype {dt}")
 
 
-def quantize_rotate(x: torch.Tensor, rot=None, codes: torch.Tensor = None, scales: torch.Tensor = None):
+def padded_rows(rows: int) -> int:
+    """Rows of a TILED operand: rows rounded up to the 256-row tile."""
+    return (rows + TILE_ROWS - 1) // TILE_ROWS * TILE_ROWS
+
+
+def tiled_bytes(rows: int, k: int):
+    """(codes bytes, scales bytes) of a TILED operand, from the library."""
+    cb, sb = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().mxfp4_tiled_bytes(rows, k, ctypes.byref(cb), ctypes.byref(sb)), "mxfp4_tiled_bytes")
+    return cb.value, sb.value
+
+
+def _out_shapes(rows: int, k: int, layout: int):
+    r = padded_rows(rows) if layout == TILED else rows
+    return (r, k // 2), (r, k // 32)
+
+
+def quantize_rotate(x: torch.Tensor, rot=None, codes: torch.Tensor = None, scales: torch.Tensor = None,
+                    layout: int = ROWMAJOR):
     """MXFP4-quantize the rows of x (fp32 or bf16, [rows, k], unit column
-    stride) with an optional block rotation.  Returns (codes [rows, k/2]
-    uint8, scales [rows, k/32] uint8)."""
+    stride) with an optional block rotation.  Returns (codes, scales) uint8:
+    [rows, k/2] and [rows, k/32] (ROWMAJOR), or the same shapes over
+    padded_rows(rows) rows holding the tiled bytes (TILED)."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, k = x.shape
+    cshape, sshape = _out_shapes(rows, k, layout)
     if codes is None:
-        codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
     if not (codes.is_contiguous() and scales.is_contiguous()):
         raise ValueError("codes and scales must be contiguous")
+    if tuple(codes.shape) != cshape or tuple(scales.shape) != sshape:
+        raise ValueError(f"codes/scales must be {cshape} / {sshape}")
     desc, _keep = _rot_desc(rot, x.device)
     st = lib().mxfp4_quantize_rotate(
         x.data_ptr(), _dtype_code(x.dtype), rows, k, x.stride(0),
-        ctypes.byref(desc) if desc is not None else None,
+        ctypes.byref(desc) if desc is not None else None, layout,
         codes.data_ptr(), scales.data_ptr(), _stream(x.device))
     _check(st, "mxfp4_quantize_rotate")
     return codes, scales
 
 
 def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
-         out_dtype=torch.bfloat16, y: torch.Tensor = None) -> torch.Tensor:
-    """Y = A * B^T with A [m, k] and B [n, k] in packed MXFP4 (codes [*, k/2],
-    scales [*, k/32]); fp32 accumulation, fp32 or bf16 output [m, n]."""
-    m, n, k = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
-    if b_codes.shape[1] * 2 != k or a_scales.shape != (m, k // 32) or b_scales.shape != (n, k // 32):
-        raise ValueError("operand shapes disagree")
+         out_dtype=torch.bfloat16, y: torch.Tensor = None, layout: int = ROWMAJOR, m: int = None, n: int = None):
+    """Y = A * B^T with A [m, k] and B [n, k] in packed MXFP4 (both in
+    `layout`); fp32 accumulation, fp32 or bf16 output [m, n].  For TILED
+    operands the real row counts come from y, or from m and n."""
+    k = a_codes.shape[1] * 2
+    if y is not None:
+        m, n = y.shape
+    if m is None:
+        m = a_codes.shape[0]
+    if n is None:
+        n = b_codes.shape[0]
+    for rows, c, sc, name in ((m, a_codes, a_scales, "A"), (n, b_codes, b_scales, "B")):
+        cshape, sshape = _out_shapes(rows, k, layout)
+        if tuple(c.shape) != cshape or tuple(sc.shape) != sshape:
+            raise ValueError(f"operand {name}: codes/scales must be {cshape} / {sshape}")
     for t in (a_codes, a_scales, b_codes, b_scales):
         if t.dtype != torch.uint8 or not t.is_contiguous():
             raise ValueError("codes and scales must be contiguous uint8 tensors")
@@ -172,28 +213,65 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b
     if y.dim() != 2 or y.shape != (m, n) or y.stride(1) != 1:
         raise ValueError("y must be [m, n] with unit column stride")
     st = lib().mxfp4_gemm(a_codes.data_ptr(), a_scales.data_ptr(), m,
-                          b_codes.data_ptr(), b_scales.data_ptr(), n, k,
+                          b_codes.data_ptr(), b_scales.data_ptr(), n, k, layout,
                           y.data_ptr(), _dtype_code(y.dtype), y.stride(0), _stream(a_codes.device))
     _check(st, "mxfp4_gemm")
     return y
 
 
 def linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, rot=None,
-           out_dtype=torch.bfloat16, y: torch.Tensor = None) -> torch.Tensor:
+           out_dtype=torch.bfloat16, y: torch.Tensor = None, layout: int = ROWMAJOR, n: int = None) -> torch.Tensor:
     """One W4A4 MXFP4 linear layer: online quantization of x (with the
     activation side of `rot`) followed by the MXFP4 GEMM against
-    pre-quantized weights."""
-    a_codes, a_scales = quantize_rotate(x, rot)
-    return gemm(a_codes, a_scales, w_codes, w_scales, out_dtype, y)
+    pre-quantized weights (in the same layout; n = weight rows for TILED)."""
+    a_codes, a_scales = quantize_rotate(x, rot, layout=layout)
+    return gemm(a_codes, a_scales, w_codes, w_scales, out_dtype, y, layout=layout, m=x.shape[0], n=n)
 
 
-def quantize_weight(w: torch.Tensor, rot=None):
+def quantize_weight(w: torch.Tensor, rot=None, layout: int = ROWMAJOR):
     """Offline weight quantization with the weight side of `rot`: the same
     Hadamard-32 (it is its own inverse-transpose), or the Kronecker factors
     (A^-T, B^-T), so that each block dot product is preserved."""
     if isinstance(rot, Kron):
         rot = rot.weight_side()
-    return quantize_rotate(w, rot)
+    return quantize_rotate(w, rot, layout=layout)
+
+
+def _tiled_index(rows_pad: int, k: int):
+    """For each byte of the tiled codes and scales, the flat index of the
+    same byte in row-major codes [rows_pad, k/2] and scales [rows_pad, k/32]."""
+    T, S = rows_pad // TILE_ROWS, k // TILE_K
+    t, s, r, p, b = np.meshgrid(np.arange(T), np.arange(S), np.arange(TILE_ROWS), np.arange(4),
+                                np.arange(16), indexing="ij")
+    row = t * TILE_ROWS + r
+    c = p ^ (((r >> 1) ^ (r >> 2)) & 3)          # block of the stage stored at position p
+    cidx = row * (k // 2) + (4 * s + c) * 16 + b
+    t2, s2, r2, c2 = np.meshgrid(np.arange(T), np.arange(S), np.arange(TILE_ROWS), np.arange(4), indexing="ij")
+    sidx = (t2 * TILE_ROWS + r2) * (k // 32) + 4 * s2 + c2
+    return cidx.reshape(-1), sidx.reshape(-1)
+
+
+def tile_host(codes: np.ndarray, scales: np.ndarray):
+    """Row-major (codes [rows, k/2], scales [rows, k/32]) -> TILED arrays of
+    padded_rows(rows) rows (padding rows zero)."""
+    rows, k = codes.shape[0], codes.shape[1] * 2
+    rp = padded_rows(rows)
+    c = np.zeros((rp, k // 2), np.uint8)
+    sc = np.zeros((rp, k // 32), np.uint8)
+    c[:rows], sc[:rows] = codes, scales
+    ci, si = _tiled_index(rp, k)
+    return c.reshape(-1)[ci].reshape(rp, k // 2), sc.reshape(-1)[si].reshape(rp, k // 32)
+
+
+def untile_host(tcodes: np.ndarray, tscales: np.ndarray, rows: int):
+    """TILED arrays -> row-major (codes [rows, k/2], scales [rows, k/32])."""
+    rp, k = tcodes.shape[0], tcodes.shape[1] * 2
+    ci, si = _tiled_index(rp, k)
+    c = np.empty(rp * k // 2, np.uint8)
+    sc = np.empty(rp * k // 32, np.uint8)
+    c[ci] = np.ascontiguousarray(tcodes).reshape(-1)
+    sc[si] = np.ascontiguousarray(tscales).reshape(-1)
+    return c.reshape(rp, k // 2)[:rows], sc.reshape(rp, k // 32)[:rows]
 
 
 def inverse_transpose(m: np.ndarray) -> np.ndarray:

@@ -31,11 +31,24 @@ MXFP4_API const char* mxfp4_status_string(int32_t status) {
   }
 }
 
+MXFP4_API mxfp4_status mxfp4_tiled_bytes(int64_t rows, int64_t k, int64_t* codes_bytes,
+                                         int64_t* scales_bytes) {
+  if (codes_bytes == nullptr || scales_bytes == nullptr || rows < 0 || k <= 0 || (k % mxfp4::kTileK) != 0)
+    return MXFP4_ERR_INVALID_ARG;
+  if (rows >= kMaxDim || k >= kMaxDim) return MXFP4_ERR_UNSUPPORTED;
+  const int64_t rows_pad = (rows + mxfp4::kTileRows - 1) / mxfp4::kTileRows * mxfp4::kTileRows;
+  *codes_bytes = rows_pad * (k / 2);
+  *scales_bytes = rows_pad * (k / 32);
+  return MXFP4_OK;
+}
+
 MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype, int64_t rows, int64_t k,
-                                             int64_t ld_x, const mxfp4_rotation* rot,
+                                             int64_t ld_x, const mxfp4_rotation* rot, int32_t layout,
                                              uint8_t* codes, uint8_t* scales, void* stream) {
   if (x_dtype != MXFP4_F32 && x_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
-  if (rows < 0 || k <= 0 || (k % 32) != 0 || ld_x < k) return MXFP4_ERR_INVALID_ARG;
+  if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
+  const bool tiled = layout == MXFP4_LAYOUT_TILED;
+  if (rows < 0 || k <= 0 || (k % (tiled ? mxfp4::kTileK : 32)) != 0 || ld_x < k) return MXFP4_ERR_INVALID_ARG;
   int32_t kind = MXFP4_ROT_NONE, p = 0, q = 0;
   const float *fa = nullptr, *fb = nullptr;
   if (rot != nullptr) {
@@ -57,7 +70,9 @@ MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype, int
   if (x == nullptr || codes == nullptr || scales == nullptr) return MXFP4_ERR_INVALID_ARG;
   const int64_t elem = (x_dtype == MXFP4_BF16) ? 2 : 4;
   if (!aligned(x, 16) || ((ld_x * elem) % 16) != 0 || !aligned(codes, 16)) return MXFP4_ERR_UNSUPPORTED;
-  if (rows * (k / 32) >= (int64_t(1) << 31)) return MXFP4_ERR_UNSUPPORTED;
+  if (tiled && !aligned(scales, 4)) return MXFP4_ERR_UNSUPPORTED;
+  const int64_t rows_pad = tiled ? (rows + mxfp4::kTileRows - 1) / mxfp4::kTileRows * mxfp4::kTileRows : rows;
+  if (rows_pad * (k / 32) >= (int64_t(1) << 31)) return MXFP4_ERR_UNSUPPORTED;
 
   mxfp4::QuantArgs a;
   a.x = x;
@@ -71,20 +86,26 @@ MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype, int
   a.fb = fb;
   a.codes = codes;
   a.scales = scales;
+  a.tiled = tiled;
+  a.rows_pad = static_cast<uint32_t>(rows_pad);
   return from_hip(mxfp4::launch_quantize(a, x_dtype == MXFP4_BF16, static_cast<hipStream_t>(stream)));
 }
 
 MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, int64_t k,
-                                  void* y, int32_t y_dtype, int64_t ld_y, void* stream) {
+                                  int32_t layout, void* y, int32_t y_dtype, int64_t ld_y, void* stream) {
   if (y_dtype != MXFP4_F32 && y_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
-  if (m < 0 || n < 0 || k <= 0 || (k % 32) != 0 || ld_y < n) return MXFP4_ERR_INVALID_ARG;
+  if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
+  const bool tiled = layout == MXFP4_LAYOUT_TILED;
+  if (m < 0 || n < 0 || k <= 0 || (k % (tiled ? mxfp4::kTileK : 32)) != 0 || ld_y < n)
+    return MXFP4_ERR_INVALID_ARG;
   if (m == 0 || n == 0) return MXFP4_OK;
   if (a_codes == nullptr || a_scales == nullptr || b_codes == nullptr || b_scales == nullptr ||
       y == nullptr)
     return MXFP4_ERR_INVALID_ARG;
   if (m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return MXFP4_ERR_UNSUPPORTED;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return MXFP4_ERR_UNSUPPORTED;
+  if (tiled && (!aligned(a_scales, 4) || !aligned(b_scales, 4))) return MXFP4_ERR_UNSUPPORTED;
   const int64_t ybytes = (y_dtype == MXFP4_BF16) ? 2 : 4;
   if (!aligned(y, ybytes)) return MXFP4_ERR_UNSUPPORTED;
 
@@ -99,6 +120,7 @@ MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
   g.y = y;
   g.ld_y = ld_y;
   g.y_bf16 = (y_dtype == MXFP4_BF16);
+  g.tiled = tiled;
   return from_hip(mxfp4::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 

@@ -43,9 +43,18 @@
 //    and workgroup b, which the dispatcher places on XCD b % 8, takes logical
 //    tiles so that the 32 workgroups of one XCD work on one compact 4 x 8
 //    block of tiles at a time and share its operand panels in that XCD's L2.
-//  * Rows beyond M or N are clamped to a valid row (never stored).  K must be
-//    a multiple of 128 (the host routes other shapes to the general kernel).
+//  * Row-major operands: rows beyond M or N are clamped to a valid row (never
+//    stored).  Tiled operands (the library's GEMM-native layout) hold each
+//    stage of each 256-row tile as the exact LDS image, so every load is one
+//    contiguous KiB of codes or 256 bytes of scales; their padding rows are
+//    zero.  K must be a multiple of 128 (the host routes other row-major
+//    shapes to the general kernel).
 #include "internal.h"
+
+#ifndef MXFP4_GEMM_WN
+#define MXFP4_GEMM_WN 2
+#define MXFP4_GEMM_WM 4
+#endif
 
 namespace mxfp4 {
 namespace {
@@ -60,12 +69,8 @@ constexpr int KS = 128;                      // K elements per stage
 constexpr int RB = KS / 2;                   // code bytes per row per stage
 constexpr int ROWS = BN + BM;                // rows per stage: W then X
 constexpr int NBUF = 4;                      // LDS ring depth
-constexpr int NT = 256;                      // 4 waves
 constexpr int CODE_BYTES = ROWS * RB;        // 32 KiB
 constexpr int STAGE_BYTES = CODE_BYTES + ROWS * 4;
-constexpr int CODE_LOADS = CODE_BYTES / 1024 / 4;   // per wave, 16 B per lane
-constexpr int SCALE_LOADS = ROWS * 4 / 256 / 4;     // per wave, 4 B per lane
-constexpr int LOADS_PER_STAGE = CODE_LOADS + SCALE_LOADS;
 constexpr int GROUP_M = 4;
 
 static_assert(NBUF * STAGE_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
@@ -106,7 +111,7 @@ __device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int
 // still in flight (vector memory loads of one wave complete in order, so a
 // count that only covers the later stages' loads is enough even with stores
 // outstanding).
-template <int PENDING>
+template <int PENDING, int LOADS_PER_STAGE>
 __device__ __forceinline__ void wait_stages() {
   // s_waitcnt simm16 on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
   constexpr int n = PENDING * LOADS_PER_STAGE;
@@ -114,9 +119,21 @@ __device__ __forceinline__ void wait_stages() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
+// WN x WM waves; each wave owns a (BN / WN) x (BM / WM) block of the tile as
+// FN x FM fragments of 32 x 32.
+constexpr int WN = MXFP4_GEMM_WN, WM = MXFP4_GEMM_WM;
+constexpr int NT = 64 * WN * WM;
+
 template <bool BF16OUT>
-__global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles_m, int tiles_n,
-                                                           int grid, int xcd_remap, int y_vec) {
+__global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles_m, int tiles_n, int grid,
+                                                           int xcd_remap, int y_vec) {
+  constexpr int NW = WN * WM;
+  constexpr int FN = BN / WN / 32, FM = BM / WM / 32;
+  constexpr int CODE_LOADS = CODE_BYTES / 1024 / NW;   // per wave, 16 B per lane
+  constexpr int SCALE_LOADS = ROWS * 4 / 256 / NW;     // per wave, 4 B per lane
+  constexpr int LPS = CODE_LOADS + SCALE_LOADS;
+  constexpr int CODE_LOADS_B = CODE_LOADS / 2;         // issued during sub-step 0
+  static_assert(CODE_LOADS >= 1 && SCALE_LOADS >= 1, "wave count");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE_BYTES];
 
   const int ntiles = tiles_m * tiles_n;
@@ -129,46 +146,58 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
   const int total = ((ntiles - slot + grid - 1) / grid) * nk;
   const uint32_t kbytes = (uint32_t)g.k / 2, kblocks = (uint32_t)g.k / 32;
 
-  // ---- direct LDS load plan: waves 0, 1 load weight rows, waves 2, 3 activation rows
-  const bool w_side = wave < 2;
+  // ---- direct LDS load plan: the first half of the waves loads weight rows,
+  // the second half activation rows; wave w fills stage rows
+  // [16 * CODE_LOADS * w, 16 * CODE_LOADS * (w + 1)).
+  const bool w_side = wave < NW / 2;
   const uint8_t* cbase = w_side ? g.b_codes : g.a_codes;
   const uint8_t* sbase = w_side ? g.b_scales : g.a_scales;
   const int lim = (w_side ? g.n : g.m) - 1;
-  const int half = wave & 1;
+  const int part = wave % (NW / 2);
   uint32_t coff[CODE_LOADS], soff[SCALE_LOADS];
+  // Row-major operands: each load takes 16 rows x 64 bytes (rows clamped to
+  // the last valid row).  Tiled operands: each load takes one contiguous KiB
+  // (codes) or 256 bytes (scales) that already hold the LDS image.
+  const bool tiled = g.tiled;
+  const uint32_t nstage = (uint32_t)nk;
   auto plan = [&](int j) {   // j-th tile of this workgroup
     int tm, tn;
     tile_coords(j * grid + slot, tiles_m, tiles_n, tm, tn);
-    const int r0 = w_side ? tn * BN : tm * BM;
+    const int tile = w_side ? tn : tm;
+    const int r0 = tile * (w_side ? BN : BM);
 #pragma unroll
     for (int i = 0; i < CODE_LOADS; ++i) {
-      const int row = 16 * (CODE_LOADS * half + i) + (lane >> 2);   // row within this side
-      const uint32_t grow = (uint32_t)min(r0 + row, lim);
-      coff[i] = grow * kbytes + 16u * (uint32_t)((lane & 3) ^ swz(row));
+      const int rgp = CODE_LOADS * part + i;                   // 16-row group within this side
+      if (tiled) {
+        coff[i] = (uint32_t)tile * nstage * (16 * 1024) + rgp * 1024 + lane * 16;
+      } else {
+        const int row = 16 * rgp + (lane >> 2);
+        const uint32_t grow = (uint32_t)min(r0 + row, lim);
+        coff[i] = grow * kbytes + 16u * (uint32_t)((lane & 3) ^ swz(row));
+      }
     }
 #pragma unroll
     for (int i = 0; i < SCALE_LOADS; ++i) {
-      const int row = 64 * (SCALE_LOADS * half + i) + lane;
-      soff[i] = (uint32_t)min(r0 + row, lim) * kblocks;
+      const int row = 64 * (SCALE_LOADS * part + i) + lane;
+      soff[i] = tiled ? (uint32_t)tile * nstage * 1024 + row * 4 : (uint32_t)min(r0 + row, lim) * kblocks;
     }
   };
+  const uint32_t cstride = tiled ? 16 * 1024 : RB, sstride = tiled ? 1024 : 4;   // bytes per stage
   // Issue state: tile ij of this workgroup, stage ikt within it, ring slot
   // ibuf.  The loads of one stage are issued in pieces spread through the
-  // MFMA stream (issue_codes / issue_scales), so that the four waves never
-  // stall together on the texture unit; advance() then moves to the next
-  // stage.
+  // MFMA stream, and advance() moves to the next stage.
   int ij = 0, ikt = 0, ibuf = 0;
   plan(0);
   auto issue_codes = [&](int i0, int i1) {
     uint8_t* dst = lds + ibuf * STAGE_BYTES;
-    const uint8_t* cb = cbase + ikt * RB;
+    const uint8_t* cb = cbase + ikt * cstride;
 #pragma unroll
     for (int i = i0; i < i1; ++i)
       __builtin_amdgcn_global_load_lds(cb + coff[i], dst + (CODE_LOADS * wave + i) * 1024, 16, 0, 0);
   };
   auto issue_scales = [&]() {
     uint8_t* dst = lds + ibuf * STAGE_BYTES;
-    const uint8_t* sb = sbase + ikt * 4;
+    const uint8_t* sb = sbase + ikt * sstride;
 #pragma unroll
     for (int i = 0; i < SCALE_LOADS; ++i)
       __builtin_amdgcn_global_load_lds(sb + soff[i],
@@ -182,31 +211,32 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
     }
   };
 
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % WN, wm = wave / WN;
   const int lr = lane & 31, lg = lane >> 5;
-  // LDS byte offsets of this lane's fragment rows (stage-relative)
-  int wrow[4], xrow[4];
+  // stage rows of this lane's fragments
+  int wrow[FN], xrow[FM];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    wrow[f] = wn * 128 + 32 * f + lr;
-    xrow[f] = BN + wm * 128 + 32 * f + lr;
-  }
+  for (int f = 0; f < FN; ++f) wrow[f] = wn * (BN / WN) + 32 * f + lr;
+#pragma unroll
+  for (int f = 0; f < FM; ++f) xrow[f] = BN + wm * (BM / WM) + 32 * f + lr;
   // Lane group g takes blocks 2g, 2g + 1 of a stage: a 16-bit load of the
   // row's scale bytes 2g, 2g + 1 leaves the sub-step s byte at op_sel = s.
-  auto load_scales = [&](const uint8_t* sbuf, uint32_t (&sw)[4], uint32_t (&sx)[4]) {
+  auto load_scales = [&](const uint8_t* sbuf, uint32_t (&sw)[FN], uint32_t (&sx)[FM]) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < FN; ++f)
       sw[f] = *reinterpret_cast<const uint16_t*>(sbuf + CODE_BYTES + 4 * wrow[f] + 2 * lg);
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
       sx[f] = *reinterpret_cast<const uint16_t*>(sbuf + CODE_BYTES + 4 * xrow[f] + 2 * lg);
-    }
   };
-  auto load_frags = [&](const uint8_t* sbuf, int s, u32x4 (&wf)[4], u32x4 (&xf)[4]) {
+  auto load_frags = [&](const uint8_t* sbuf, int s, u32x4 (&wf)[FN], u32x4 (&xf)[FM]) {
     const int c = 2 * lg + s;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < FN; ++f)
       wf[f] = *reinterpret_cast<const u32x4*>(sbuf + wrow[f] * RB + 16 * (c ^ swz(wrow[f])));
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
       xf[f] = *reinterpret_cast<const u32x4*>(sbuf + xrow[f] * RB + 16 * (c ^ swz(xrow[f])));
-    }
   };
 
   // The ring always has NBUF - 1 stages in flight: one stage is issued per
@@ -220,31 +250,32 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
   }
 
   // stage 0: wait for it, then load its scales and first fragments
-  wait_stages<NBUF - 2>();
+  wait_stages<NBUF - 2, LPS>();
   __builtin_amdgcn_s_barrier();
-  uint32_t sw[4], sx[4];
-  u32x4 wa[4], xa[4];
+  uint32_t sw[FN], sx[FM];
+  u32x4 wa[FN], xa[FM];
   load_scales(lds, sw, sx);
   load_frags(lds, 0, wa, xa);
 
+  constexpr int NRD = FN + FM;                  // fragment reads per sub-step
   int cbuf = 0;   // ring slot of the stage being computed
   for (int j = 0; j * nk < total; ++j) {
-    v16f acc[4][4];
+    v16f acc[FN][FM];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < FN; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < FM; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
 
     for (int kt = 0; kt < nk; ++kt) {
+      advance();   // to stage it + NBUF - 1 (its branch stays out of the MFMA block)
       // Stage it + 1 is loaded once this wave's loads of it are done and every
       // wave has passed the barrier.  The barrier also guarantees that all
       // waves have finished reading stage it - 1, whose slot this iteration's
       // loads overwrite.  No fence: a release fence on LDS would also wait for
       // the loads still in flight.
-      advance();   // to stage it + NBUF - 1 (its branch stays out of the MFMA block)
-      wait_stages<NBUF - 3>();
+      wait_stages<NBUF - 3, LPS>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
 
@@ -252,60 +283,56 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
       cbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;
       const uint8_t* nbuf = lds + cbuf * STAGE_BYTES;
 
-      // sub-step 0 MFMAs, interleaved with the sub-step 1 reads and half of
+      // sub-step 0 MFMAs, interleaved with the sub-step 1 reads and part of
       // the loads of stage it + NBUF - 1
-      u32x4 wb[4], xb[4];
+      u32x4 wb[FN], xb[FM];
       load_frags(sbuf, 1, wb, xb);
-      issue_codes(0, 4);
+      issue_codes(0, CODE_LOADS_B);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < FN; ++a)
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) acc[a][bb] = mma<0>(wa[a], xa[bb], acc[a][bb], sw[a], sx[bb]);
+        for (int bb = 0; bb < FM; ++bb) acc[a][bb] = mma<0>(wa[a], xa[bb], acc[a][bb], sw[a], sx[bb]);
       // one MFMA first (its wait then covers only older reads), the reads
       // early (they feed sub-step 1), then the loads between MFMAs
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NRD / 2; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
       }
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
+      for (int i = 0; i < CODE_LOADS_B; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // 1 global load
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // 3 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
       }
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);     // 1 global load
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // 2 MFMA
 
       // sub-step 1 MFMAs, interleaved with the next stage's scale and
       // sub-step 0 reads (after the last stage these read a slot that is
-      // never used) and the other half of the loads
-      uint32_t sw1[4], sx1[4];
+      // never used) and the rest of the loads
+      uint32_t sw1[FN], sx1[FM];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        sw1[f] = sw[f];
-        sx1[f] = sx[f];
-      }
+      for (int f = 0; f < FN; ++f) sw1[f] = sw[f];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) sx1[f] = sx[f];
       load_scales(nbuf, sw, sx);
       load_frags(nbuf, 0, wa, xa);
-      issue_codes(4, CODE_LOADS);
+      issue_codes(CODE_LOADS_B, CODE_LOADS);
       issue_scales();
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < FN; ++a)
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) acc[a][bb] = mma<1>(wb[a], xb[bb], acc[a][bb], sw1[a], sx1[bb]);
+        for (int bb = 0; bb < FM; ++bb) acc[a][bb] = mma<1>(wb[a], xb[bb], acc[a][bb], sw1[a], sx1[bb]);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NRD; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
       }
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
+      for (int i = 0; i < LPS - CODE_LOADS_B; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // 1 global load
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // last MFMA
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -313,14 +340,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
     int tm, tn;
     tile_coords(j * grid + slot, tiles_m, tiles_n, tm, tn);
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int m = tm * BM + wm * 128 + 32 * bb + lr;
+    for (int bb = 0; bb < FM; ++bb) {
+      const int m = tm * BM + wm * (BM / WM) + 32 * bb + lr;
       if (m >= g.m) continue;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
+      for (int a = 0; a < FN; ++a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int n = tn * BN + wn * 128 + 32 * a + 8 * t + 4 * lg;
+          const int n = tn * BN + wn * (BN / WN) + 32 * a + 8 * t + 4 * lg;
           const float v0 = acc[a][bb][4 * t], v1 = acc[a][bb][4 * t + 1];
           const float v2 = acc[a][bb][4 * t + 2], v3 = acc[a][bb][4 * t + 3];
           if constexpr (BF16OUT) {
@@ -368,8 +395,9 @@ int cu_count() {
 }  // namespace
 
 bool gemm_large_supported(const GemmArgs& g) {
+  const int64_t m = (g.m + BM - 1) / BM * BM, n = (g.n + BN - 1) / BN * BN;   // padded rows
   return (g.k % KS) == 0 && ((uintptr_t)g.a_scales % 4) == 0 && ((uintptr_t)g.b_scales % 4) == 0 &&
-         (int64_t)g.m * (g.k / 2) < (int64_t(1) << 32) && (int64_t)g.n * (g.k / 2) < (int64_t(1) << 32);
+         m * (g.k / 2) < (int64_t(1) << 32) && n * (g.k / 2) < (int64_t(1) << 32);
 }
 
 hipError_t launch_gemm_large(const GemmArgs& g, hipStream_t s) {

@@ -17,7 +17,12 @@ struct QuantArgs {
   const float* fb;     // q x q
   uint8_t* codes;
   uint8_t* scales;
+  bool tiled;          // MXFP4_LAYOUT_TILED outputs (nblk_row % 4 == 0)
+  uint32_t rows_pad;   // rows rounded up to the 256-row tile (tiled only)
 };
+
+constexpr int kTileRows = 256;       // rows per tile of the tiled layout
+constexpr int kTileK = 128;          // K elements per stage of the tiled layout
 
 hipError_t launch_quantize(const QuantArgs& a, bool bf16, hipStream_t s);
 
@@ -30,12 +35,14 @@ struct GemmArgs {
   void* y;
   int64_t ld_y;
   bool y_bf16;
+  bool tiled;               // both operands in MXFP4_LAYOUT_TILED
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
 // Large-tile persistent kernel (gemm_large.hip): K a multiple of 128,
-// 4-byte aligned scale pointers, operand code bytes below 4 GiB.
+// 4-byte aligned scale pointers, operand code bytes below 4 GiB; the only
+// kernel for tiled operands.
 bool gemm_large_supported(const GemmArgs& a);
 hipError_t launch_gemm_large(const GemmArgs& a, hipStream_t s);
 

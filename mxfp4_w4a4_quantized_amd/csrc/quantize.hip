@@ -102,15 +102,52 @@ __device__ __forceinline__ int slab_swz(int blk) {
   return CPB == 4 ? (blk >> 2) & 3 : (blk >> 1) & 7;
 }
 
+// Tiled-layout chunk swizzle (the GEMM's LDS bank swizzle, baked into the
+// tiled codes): block c of a stage sits at 16-byte position c ^ swz(r) of
+// row r's 64 bytes.
+__device__ __forceinline__ int tiled_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
 // rot: 0 none, 1 Hadamard-32, 2 Kronecker (P x Q)
+//
+// Work split: every wave quantizes 64 blocks.  Row-major output: 64
+// consecutive blocks in row-major block order.  Tiled output: the 4 blocks of
+// one 128-element stage in 16 consecutive rows, so the wave's code stores are
+// one contiguous KiB of the tiled layout; padding rows load as zeros and
+// store zero codes and scales.
 template <bool BF16, int ROT, int P, int Q>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int dense) {
   constexpr int CPB = BF16 ? 4 : 8;   // 16-byte chunks per 32-element block
   __shared__ u32x4 slab[kThreads / 64][64 * CPB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t wid = blockIdx.x * (kThreads / 64) + wave;   // global wave index
   const uint32_t nblk = a.rows * a.nblk_row;
-  const uint32_t wb0 = (blockIdx.x * (kThreads / 64) + wave) * 64;   // first block of this wave
-  if (wb0 >= nblk) return;
+  const uint32_t nstage = a.nblk_row / 4;
+  uint32_t wb0 = 0, rg = 0, st = 0;
+  if (a.tiled) {
+    rg = wid / nstage;
+    st = wid - rg * nstage;
+    if (rg * 16 >= a.rows_pad) return;
+  } else {
+    wb0 = wid * 64;
+    if (wb0 >= nblk) return;
+  }
+  // (row, block column) of local block bl of this wave; false if outside X
+  auto locate = [&](int bl, uint32_t& row, uint32_t& col) -> bool {
+    if (a.tiled) {
+      row = rg * 16 + (bl >> 2);
+      col = 4 * st + (bl & 3);
+      return row < a.rows;
+    }
+    const uint32_t g = wb0 + bl;
+    if (dense) {
+      row = 0;
+      col = g;   // row-contiguous blocks: g * 32 elements from x
+    } else {
+      row = g / a.nblk_row;
+      col = g - row * a.nblk_row;
+    }
+    return g < nblk;
+  };
   const int esz = BF16 ? 2 : 4;
   const uint8_t* x = static_cast<const uint8_t*>(a.x);
 
@@ -119,17 +156,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
 #pragma unroll
   for (int u = 0; u < CPB; ++u) {
     const int c = 64 * u + lane;
-    const uint32_t blk = wb0 + c / CPB;
-    const int q = c % CPB;
-    if (blk < nblk) {
-      int64_t off;
-      if (dense) {
-        off = (int64_t)blk * 32 * esz;
-      } else {
-        const uint32_t r = blk / a.nblk_row;
-        off = ((int64_t)r * a.ld_x + (int64_t)(blk - r * a.nblk_row) * 32) * esz;
-      }
-      ld[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off + 16 * q));
+    uint32_t row, col;
+    if (locate(c / CPB, row, col)) {
+      const int64_t off = ((int64_t)row * a.ld_x + (int64_t)col * 32) * esz;
+      ld[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off + 16 * (c % CPB)));
     } else {
       ld[u] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -142,8 +172,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
   }
   // The slab is private to this wave and LDS operations of one wave complete
   // in order, so the reads below see the writes above without a barrier.
-  const uint32_t gid = wb0 + lane;
-  if (gid >= nblk) return;
+  uint32_t orow, ocol;
+  const bool inside = locate(lane, orow, ocol);
+  if (!a.tiled && !inside) return;
   u32x4 q4[CPB];
 #pragma unroll
   for (int q = 0; q < CPB; ++q) q4[q] = slab[wave][lane * CPB + (q ^ slab_swz<CPB>(lane))];
@@ -193,15 +224,24 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
     acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 6], v[8 * i + 7], scale, 3);
     w[i] = acc;
   }
-  uint4* dst = reinterpret_cast<uint4*>(a.codes) + gid;
-  *dst = make_uint4(w[0], w[1], w[2], w[3]);   // the GEMM reads these next: keep them cached
-  a.scales[gid] = static_cast<uint8_t>(sbyte);
+  if (a.tiled) {
+    const uint32_t t = orow / kTileRows, r = orow % kTileRows, sg = ocol / 4, cb = ocol % 4;
+    const uint64_t ts = (uint64_t)t * nstage + sg;   // (tile, stage) index
+    uint4* dst = reinterpret_cast<uint4*>(a.codes + ts * (kTileRows * 64) + r * 64) + (cb ^ tiled_swz(r));
+    *dst = make_uint4(w[0], w[1], w[2], w[3]);
+    a.scales[ts * (kTileRows * 4) + r * 4 + cb] = static_cast<uint8_t>(sbyte);
+  } else {
+    const uint32_t gid = wb0 + lane;
+    uint4* dst = reinterpret_cast<uint4*>(a.codes) + gid;
+    *dst = make_uint4(w[0], w[1], w[2], w[3]);   // the GEMM reads these next: keep them cached
+    a.scales[gid] = static_cast<uint8_t>(sbyte);
+  }
 }
 
 template <bool BF16>
 hipError_t dispatch(const QuantArgs& a, hipStream_t s) {
-  const uint32_t nblk = a.rows * a.nblk_row;
-  const dim3 grid((nblk + kThreads - 1) / kThreads), block(kThreads);
+  const uint64_t blocks = (uint64_t)(a.tiled ? a.rows_pad : a.rows) * a.nblk_row;   // 64 per wave
+  const dim3 grid((uint32_t)((blocks + kThreads - 1) / kThreads)), block(kThreads);
   const int dense = a.ld_x == (int64_t)a.nblk_row * 32;
   if (a.rot == 0) {
     quantize_kernel<BF16, 0, 1, 32><<<grid, block, 0, s>>>(a, dense);

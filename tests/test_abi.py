@@ -41,7 +41,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mx.lib().mxfp4_abi_version() == 1
+    assert mx.lib().mxfp4_abi_version() == 2
     for s in range(4):
         assert mx.status_string(s).startswith("MXFP4_")
     assert "unknown" in mx.status_string(99)
@@ -57,50 +57,93 @@ def g(*args):
 
 def test_quantize_argument_errors():
     INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
-    A = ALIGNED
-    assert q(A, 7, 4, 64, 64, None, A, A, None) == INV      # bad dtype
-    assert q(A, 1, 4, 48, 64, None, A, A, None) == INV      # k % 32
-    assert q(A, 1, 4, 0, 64, None, A, A, None) == INV       # k == 0
-    assert q(A, 1, -1, 64, 64, None, A, A, None) == INV     # rows < 0
-    assert q(A, 1, 4, 64, 32, None, A, A, None) == INV      # ld < k
-    assert q(NULL, 1, 4, 64, 64, None, A, A, None) == INV   # null x
-    assert q(A, 1, 4, 64, 64, None, NULL, A, None) == INV   # null codes
-    assert q(A, 1, 4, 64, 64, None, A, NULL, None) == INV   # null scales
-    assert q(NULL, 1, 0, 64, 64, None, NULL, NULL, None) == OK   # rows == 0: no-op
-    assert q(MISALIGNED, 1, 4, 64, 64, None, A, A, None) == UNS
-    assert q(A, 1, 4, 64, 68, None, A, A, None) == UNS      # bf16 row stride not 16 B
-    assert q(A, 1, 4, 64, 64, None, A + 8, A, None) == UNS  # codes not 16 B aligned
-    assert q(A, 1, 1 << 30, 4096, 4096, None, A, A, None) == UNS   # too many blocks
+    A, R, T = ALIGNED, mx.ROWMAJOR, mx.TILED
+    assert q(A, 7, 4, 64, 64, None, R, A, A, None) == INV      # bad dtype
+    assert q(A, 1, 4, 48, 64, None, R, A, A, None) == INV      # k % 32
+    assert q(A, 1, 4, 0, 64, None, R, A, A, None) == INV       # k == 0
+    assert q(A, 1, -1, 64, 64, None, R, A, A, None) == INV     # rows < 0
+    assert q(A, 1, 4, 64, 32, None, R, A, A, None) == INV      # ld < k
+    assert q(A, 1, 4, 64, 64, None, 2, A, A, None) == INV      # bad layout
+    assert q(A, 1, 4, 64, 64, None, T, A, A, None) == INV      # tiled: k % 128
+    assert q(NULL, 1, 4, 64, 64, None, R, A, A, None) == INV   # null x
+    assert q(A, 1, 4, 64, 64, None, R, NULL, A, None) == INV   # null codes
+    assert q(A, 1, 4, 64, 64, None, R, A, NULL, None) == INV   # null scales
+    assert q(NULL, 1, 0, 64, 64, None, R, NULL, NULL, None) == OK   # rows == 0: no-op
+    assert q(MISALIGNED, 1, 4, 64, 64, None, R, A, A, None) == UNS
+    assert q(A, 1, 4, 64, 68, None, R, A, A, None) == UNS      # bf16 row stride not 16 B
+    assert q(A, 1, 4, 64, 64, None, R, A + 8, A, None) == UNS  # codes not 16 B aligned
+    assert q(A, 1, 4, 128, 128, None, T, A, A + 2, None) == UNS   # tiled scales not 4 B aligned
+    assert q(A, 1, 1 << 30, 4096, 4096, None, R, A, A, None) == UNS   # too many blocks
     bad = mx.RotationDesc(9, 0, 0, 0, None, None)
-    assert q(A, 1, 4, 64, 64, ctypes.byref(bad), A, A, None) == INV
+    assert q(A, 1, 4, 64, 64, ctypes.byref(bad), R, A, A, None) == INV
     kr = mx.RotationDesc(mx.ROT_KRON, 4, 4, 0, A, A)
-    assert q(A, 1, 4, 64, 64, ctypes.byref(kr), A, A, None) == INV     # p*q != 32
+    assert q(A, 1, 4, 64, 64, ctypes.byref(kr), R, A, A, None) == INV     # p*q != 32
     kr = mx.RotationDesc(mx.ROT_KRON, 4, 8, 0, None, A)
-    assert q(A, 1, 4, 64, 64, ctypes.byref(kr), A, A, None) == INV     # null factor
+    assert q(A, 1, 4, 64, 64, ctypes.byref(kr), R, A, A, None) == INV     # null factor
     kr = mx.RotationDesc(mx.ROT_KRON, 4, 8, 1, A, A)
-    assert q(A, 1, 4, 64, 64, ctypes.byref(kr), A, A, None) == INV     # reserved != 0
+    assert q(A, 1, 4, 64, 64, ctypes.byref(kr), R, A, A, None) == INV     # reserved != 0
 
 
 def test_gemm_argument_errors():
     INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
-    A = ALIGNED
-    assert g(A, A, 4, A, A, 4, 64, A, 5, 4, None) == INV     # bad dtype
-    assert g(A, A, 4, A, A, 4, 48, A, 0, 4, None) == INV     # k % 32
-    assert g(A, A, 4, A, A, 4, 0, A, 0, 4, None) == INV      # k == 0
-    assert g(A, A, -4, A, A, 4, 64, A, 0, 4, None) == INV    # m < 0
-    assert g(A, A, 4, A, A, -4, 64, A, 0, 4, None) == INV    # n < 0
-    assert g(A, A, 4, A, A, 8, 64, A, 0, 4, None) == INV     # ld_y < n
-    assert g(NULL, A, 4, A, A, 4, 64, A, 0, 4, None) == INV
-    assert g(A, NULL, 4, A, A, 4, 64, A, 0, 4, None) == INV
-    assert g(A, A, 4, NULL, A, 4, 64, A, 0, 4, None) == INV
-    assert g(A, A, 4, A, NULL, 4, 64, A, 0, 4, None) == INV
-    assert g(A, A, 4, A, A, 4, 64, NULL, 0, 4, None) == INV
-    assert g(NULL, NULL, 0, NULL, NULL, 4, 64, NULL, 0, 4, None) == OK   # m == 0
-    assert g(NULL, NULL, 4, NULL, NULL, 0, 64, NULL, 0, 0, None) == OK   # n == 0
-    assert g(A + 4, A, 4, A, A, 4, 64, A, 0, 4, None) == UNS   # misaligned codes
-    assert g(A, A, 4, A + 8, A, 4, 64, A, 0, 4, None) == UNS
-    assert g(A, A, 4, A, A, 4, 64, A + 2, 0, 4, None) == UNS   # fp32 y misaligned
-    assert g(A, A, 1 << 30, A, A, 4, 64, A, 0, 4, None) == UNS
+    A, R, T = ALIGNED, mx.ROWMAJOR, mx.TILED
+    assert g(A, A, 4, A, A, 4, 64, R, A, 5, 4, None) == INV     # bad dtype
+    assert g(A, A, 4, A, A, 4, 48, R, A, 0, 4, None) == INV     # k % 32
+    assert g(A, A, 4, A, A, 4, 0, R, A, 0, 4, None) == INV      # k == 0
+    assert g(A, A, -4, A, A, 4, 64, R, A, 0, 4, None) == INV    # m < 0
+    assert g(A, A, 4, A, A, -4, 64, R, A, 0, 4, None) == INV    # n < 0
+    assert g(A, A, 4, A, A, 8, 64, R, A, 0, 4, None) == INV     # ld_y < n
+    assert g(A, A, 4, A, A, 4, 64, 3, A, 0, 4, None) == INV     # bad layout
+    assert g(A, A, 4, A, A, 4, 64, T, A, 0, 4, None) == INV     # tiled: k % 128
+    assert g(NULL, A, 4, A, A, 4, 64, R, A, 0, 4, None) == INV
+    assert g(A, NULL, 4, A, A, 4, 64, R, A, 0, 4, None) == INV
+    assert g(A, A, 4, NULL, A, 4, 64, R, A, 0, 4, None) == INV
+    assert g(A, A, 4, A, NULL, 4, 64, R, A, 0, 4, None) == INV
+    assert g(A, A, 4, A, A, 4, 64, R, NULL, 0, 4, None) == INV
+    assert g(NULL, NULL, 0, NULL, NULL, 4, 64, R, NULL, 0, 4, None) == OK   # m == 0
+    assert g(NULL, NULL, 4, NULL, NULL, 0, 64, R, NULL, 0, 0, None) == OK   # n == 0
+    assert g(A + 4, A, 4, A, A, 4, 64, R, A, 0, 4, None) == UNS   # misaligned codes
+    assert g(A, A, 4, A + 8, A, 4, 64, R, A, 0, 4, None) == UNS
+    assert g(A, A, 4, A, A, 4, 64, R, A + 2, 0, 4, None) == UNS   # fp32 y misaligned
+    assert g(A, A + 1, 4, A, A, 4, 128, T, A, 0, 4, None) == UNS   # tiled scales misaligned
+    assert g(A, A, 1 << 30, A, A, 4, 64, R, A, 0, 4, None) == UNS
+
+
+def test_tiled_bytes():
+    INV = mx.MXFP4_ERR_INVALID_ARG
+    assert mx.tiled_bytes(1, 128) == (256 * 64, 256 * 4)
+    assert mx.tiled_bytes(256, 3072) == (256 * 1536, 256 * 96)
+    assert mx.tiled_bytes(257, 256) == (512 * 128, 512 * 8)
+    assert mx.tiled_bytes(0, 128) == (0, 0)
+    cb, sb = ctypes.c_int64(), ctypes.c_int64()
+    assert mx.lib().mxfp4_tiled_bytes(4, 96, ctypes.byref(cb), ctypes.byref(sb)) == INV
+    assert mx.lib().mxfp4_tiled_bytes(-1, 128, ctypes.byref(cb), ctypes.byref(sb)) == INV
+    assert mx.lib().mxfp4_tiled_bytes(4, 128, None, ctypes.byref(sb)) == INV
+
+
+@pytest.mark.parametrize("rows,k", [(1, 128), (255, 256), (256, 384), (700, 512)])
+def test_host_tiling_roundtrip_and_definition(rows, k):
+    """tile_host / untile_host are inverse permutations, and the tiled bytes
+    sit where the header's layout definition puts them."""
+    rng = np.random.default_rng(rows + k)
+    c = rng.integers(0, 256, (rows, k // 2), dtype=np.uint8)
+    s = rng.integers(0, 256, (rows, k // 32), dtype=np.uint8)
+    tc, ts = mx.tile_host(c, s)
+    assert tc.shape == (mx.padded_rows(rows), k // 2) and ts.shape == (mx.padded_rows(rows), k // 32)
+    c2, s2 = mx.untile_host(tc, ts, rows)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+    flat_c, flat_s = tc.reshape(-1), ts.reshape(-1)
+    S = k // 128
+    for row in (0, rows - 1, rows // 2):
+        for blk in (0, k // 32 - 1):
+            t, r, st, cb = row // 256, row % 256, blk // 4, blk % 4
+            p = cb ^ (((r >> 1) ^ (r >> 2)) & 3)
+            base = (t * S + st) * 16384 + r * 64 + 16 * p
+            assert np.array_equal(flat_c[base:base + 16], c[row, 16 * blk:16 * blk + 16])
+            assert flat_s[(t * S + st) * 1024 + r * 4 + cb] == s[row, blk]
+    if mx.padded_rows(rows) > rows:   # padding rows are zero
+        pc, ps = mx.untile_host(tc, ts, mx.padded_rows(rows))
+        assert not pc[rows:].any() and not ps[rows:].any()
 
 
 @pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32])

@@ -128,6 +128,31 @@ def test_large_tile_strided_output():
         assert (host[:, :4] == fill).all() and (host[:, 4 + n:] == fill).all()   # no stray writes
 
 
+TILED_SHAPES = [
+    (256, 256, 128), (257, 300, 256), (1000, 520, 384), (16, 1000, 256), (96, 2048, 512),
+    (4352, 4352, 128), (2304, 4608, 384)]
+
+
+@pytest.mark.parametrize("m,n,k", TILED_SHAPES)
+def test_tiled_operands(m, n, k):
+    """Both operands in the tiled layout (tiled on the host, a byte
+    permutation), every output element checked against the oracle."""
+    rng = np.random.default_rng(m * 13 + n * 5 + k)
+    ac, as_ = workloads.random_mxfp4(rng, m, k)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+    announce("gemm tiled", m, n, k)
+    ta, tas = mx.tile_host(ac, as_)
+    tb, tbs = mx.tile_host(bc, bs)
+    dev = [to_dev(t) for t in (ta, tas, tb, tbs)]
+    y32 = mx.gemm(*dev, torch.float32, layout=mx.TILED, m=m, n=n)
+    y16 = mx.gemm(*dev, torch.bfloat16, layout=mx.TILED, m=m, n=n)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(ac, as_, bc, bs)
+    err = norm_err(y32.cpu().numpy(), ref, row_norms(ac, as_), row_norms(bc, bs))
+    assert err <= TOL, f"normalized error {err:.3e}"
+    assert np.array_equal(y16.view(torch.int16).cpu().numpy().view(np.uint16), bf16_rne(y32))
+
+
 def test_extreme_scales():
     # scale bytes near both ends of the E8M0 range (products stay finite)
     rng = np.random.default_rng(77)
@@ -209,28 +234,33 @@ def act_rot(inp):
     return None
 
 
-@pytest.mark.parametrize("name", [n for n in workloads.WORKLOADS if n != "tiny"])
-def test_full_workload_linear(name):
+@pytest.mark.parametrize("name,layout", [(n, "tiled") for n in workloads.WORKLOADS if n != "tiny"]
+                         + [("flux_up", "rowmajor")])
+def test_full_workload_linear(name, layout):
     """Full-size linear layer in the launch configuration the benchmark
-    times: device quantization of X (activation side) and W (weight side),
-    then the GEMM; operands checked bit-exact against the oracle's, outputs
-    checked on 4096 sampled elements plus the whole first and last rows and
-    columns, with the oracle computing each sampled element as one binary64
-    dot product."""
+    times (tiled layout): device quantization of X (activation side) and W
+    (weight side), then the GEMM; operands checked bit-exact against the
+    oracle's (after untiling on the host), outputs checked on 4096 sampled
+    elements plus the whole first and last rows and columns, with the oracle
+    computing each sampled element as one binary64 dot product."""
     inp = workloads.make(name)
     wl = inp["wl"]
+    lay = mx.TILED if layout == "tiled" else mx.ROWMAJOR
     bf16 = wl.x_dtype == "bf16"
     x = to_dev(inp["x"].view(np.int16)).view(torch.bfloat16) if bf16 else to_dev(inp["x"])
     w = to_dev(inp["w"])
     rot = act_rot(inp)
-    announce("linear", name, wl.m, wl.n, wl.k)
-    wc, ws = mx.quantize_weight(w, rot)
+    announce("linear", name, layout, wl.m, wl.n, wl.k)
+    wc, ws = mx.quantize_weight(w, rot, layout=lay)
     out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
-    xc, xs = mx.quantize_rotate(x, rot)
-    y32 = mx.gemm(xc, xs, wc, ws, torch.float32)
-    y = mx.gemm(xc, xs, wc, ws, out_dtype)
+    xc, xs = mx.quantize_rotate(x, rot, layout=lay)
+    y32 = mx.gemm(xc, xs, wc, ws, torch.float32, layout=lay, m=wl.m, n=wl.n)
+    y = mx.gemm(xc, xs, wc, ws, out_dtype, layout=lay, m=wl.m, n=wl.n)
     torch.cuda.synchronize()
     hxc, hxs, hwc, hws = (t.cpu().numpy() for t in (xc, xs, wc, ws))
+    if lay == mx.TILED:
+        hxc, hxs = mx.untile_host(hxc, hxs, wl.m)
+        hwc, hws = mx.untile_host(hwc, hws, wl.n)
     # operands: bit-exact against the oracle's quantizer
     orot = None if wl.rot is None else ("h32" if wl.rot == "h32" else ("kron", inp["a"], inp["b"]))
     rxc, rxs = oracle.quantize(inp["x"], rot=orot, bf16=bf16)
@@ -260,7 +290,7 @@ def test_full_workload_linear(name):
     den_b = np.array([nmap_b[j] for j in ni])
     g32 = y32[torch.from_numpy(mi).to(DEV), torch.from_numpy(ni).to(DEV)].cpu().numpy()
     err = norm_err(g32, ref, den_a, den_b)
-    print(f"[result] {name}: max normalized error {err:.3e}", flush=True)
+    print(f"[result] {name} {layout}: max normalized error {err:.3e}", flush=True)
     assert err <= TOL
     if out_dtype == torch.bfloat16:
         assert torch.equal(y.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))

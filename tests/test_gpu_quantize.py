@@ -143,6 +143,41 @@ def test_strided_input_rows():
     assert_same((c.cpu().numpy(), s.cpu().numpy()), ref, "strided")
 
 
+@pytest.mark.parametrize("rows,k,bf16,rot", [
+    (1, 128, True, None), (255, 256, True, "h32"), (300, 384, False, None), (513, 512, True, "kron"),
+    (1024, 3072, True, "h32"), (16, 4096, True, "kron")])
+def test_tiled_layout_matches_oracle(rows, k, bf16, rot):
+    """Tiled output (the GEMM-native layout): untiled on the host it must equal
+    the oracle's codes and scales bit for bit, and the padding rows must be
+    zero."""
+    rng = np.random.default_rng(rows * 3 + k)
+    x = workloads.random_blocks(rng, rows, k)
+    if bf16:
+        x = workloads.bf16_bits(x)
+    r = rand_kron(4, 8, 9) if rot == "kron" else rot
+    announce("quantize tiled", rows, k, "bf16" if bf16 else "f32", rot)
+    c, s = mx.quantize_rotate(dev_x(x, bf16), r, layout=mx.TILED)
+    torch.cuda.synchronize()
+    tc, ts = c.cpu().numpy(), s.cpu().numpy()
+    assert tc.shape == (mx.padded_rows(rows), k // 2)
+    got = mx.untile_host(tc, ts, rows)
+    ref = oracle.quantize(x, rot=oracle_rot(r), bf16=bf16)
+    assert_same(got, ref, f"tiled {rows}x{k}")
+    pc, ps = mx.untile_host(tc, ts, mx.padded_rows(rows))
+    assert not pc[rows:].any() and not ps[rows:].any()
+
+
+def test_tiled_strided_input():
+    rng = np.random.default_rng(6)
+    full = workloads.bf16_bits(workloads.random_blocks(rng, 70, 640))
+    x = dev_x(full, True)[:, :256]                   # ld_x = 640 > k = 256
+    announce("quantize tiled strided", x.shape, x.stride())
+    c, s = mx.quantize_rotate(x, "h32", layout=mx.TILED)
+    got = mx.untile_host(c.cpu().numpy(), s.cpu().numpy(), 70)
+    ref = oracle.quantize(np.ascontiguousarray(full[:, :256]), rot="h32", bf16=True)
+    assert_same(got, ref, "tiled strided")
+
+
 def test_zero_rows_is_noop():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
     c, s = mx.quantize_rotate(x)
