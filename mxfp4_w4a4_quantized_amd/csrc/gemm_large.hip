@@ -53,7 +53,7 @@
 
 #ifndef MXFP4_GEMM_WN
 #define MXFP4_GEMM_WN 2
-#define MXFP4_GEMM_WM 4
+#define MXFP4_GEMM_WM 2
 #endif
 
 namespace mxfp4 {
@@ -119,6 +119,28 @@ __device__ __forceinline__ void wait_stages() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
+// Scheduling pattern of one MFMA sub-step: MF MFMAs; RD LDS reads issued two
+// per MFMA from the second MFMA on (they feed the next sub-step); VM global
+// loads spread evenly over the MFMAs after the reads, so that the four waves'
+// loads reach the texture unit at a steady rate.
+template <int MF, int RD, int VM, int I = 0, int RDL = RD, int VML = VM>
+__device__ __forceinline__ void sched_substep() {
+  if constexpr (I < MF) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
+    constexpr int rd = (I >= 1 && RDL > 0) ? (RDL >= 2 ? 2 : 1) : 0;
+    if constexpr (rd > 0) __builtin_amdgcn_sched_group_barrier(0x100, rd, 0);   // LDS reads
+    constexpr int from = (RD + 1) / 2 + 1;
+    constexpr int span = MF - from > 0 ? MF - from : 1;
+    constexpr int vm = (I >= from) ? ((I - from + 1) * VM) / span - ((I - from) * VM) / span : 0;
+    constexpr int vmc = vm < VML ? vm : VML;
+    if constexpr (vmc > 0) __builtin_amdgcn_sched_group_barrier(0x010, vmc, 0);  // global loads
+    sched_substep<MF, RD, VM, I + 1, RDL - rd, VML - vmc>();
+  } else {
+    if constexpr (RDL > 0) __builtin_amdgcn_sched_group_barrier(0x100, RDL, 0);
+    if constexpr (VML > 0) __builtin_amdgcn_sched_group_barrier(0x010, VML, 0);
+  }
+}
+
 // WN x WM waves; each wave owns a (BN / WN) x (BM / WM) block of the tile as
 // FN x FM fragments of 32 x 32.
 constexpr int WN = MXFP4_GEMM_WN, WM = MXFP4_GEMM_WM;
@@ -145,6 +167,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
   const int nk = g.k / KS;
   const int total = ((ntiles - slot + grid - 1) / grid) * nk;
   const uint32_t kbytes = (uint32_t)g.k / 2, kblocks = (uint32_t)g.k / 32;
+  // output rows start 16-byte aligned: the staged epilogue's 16-byte stores
+  const bool y_st = ((uintptr_t)g.y % 16) == 0 && ((g.ld_y * (BF16OUT ? 2 : 4)) % 16) == 0;
 
   // ---- direct LDS load plan: the first half of the waves loads weight rows,
   // the second half activation rows; wave w fills stage rows
@@ -292,19 +316,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
       for (int a = 0; a < FN; ++a)
 #pragma unroll
         for (int bb = 0; bb < FM; ++bb) acc[a][bb] = mma<0>(wa[a], xa[bb], acc[a][bb], sw[a], sx[bb]);
-      // one MFMA first (its wait then covers only older reads), the reads
-      // early (they feed sub-step 1), then the loads between MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
-#pragma unroll
-      for (int i = 0; i < NRD / 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      }
-#pragma unroll
-      for (int i = 0; i < CODE_LOADS_B; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // 1 global load
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      }
+      sched_substep<FN * FM, NRD, CODE_LOADS_B>();
 
       // sub-step 1 MFMAs, interleaved with the next stage's scale and
       // sub-step 0 reads (after the last stage these read a slot that is
@@ -322,23 +334,59 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
       for (int a = 0; a < FN; ++a)
 #pragma unroll
         for (int bb = 0; bb < FM; ++bb) acc[a][bb] = mma<1>(wb[a], xb[bb], acc[a][bb], sw1[a], sx1[bb]);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
-#pragma unroll
-      for (int i = 0; i < NRD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      }
-#pragma unroll
-      for (int i = 0; i < LPS - CODE_LOADS_B; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // 1 global load
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      }
+      sched_substep<FN * FM, 2 * NRD, LPS - CODE_LOADS_B>();
       __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- epilogue of this workgroup's j-th tile
     int tm, tn;
     tile_coords(j * grid + slot, tiles_m, tiles_n, tm, tn);
+    if constexpr (WN == 2 && WM == 2) {
+      // Interior tiles: stage each wave's 128 x 128 output block through the
+      // ring slot of the stage just computed (free until the next issue,
+      // which follows the next barrier), 32 rows x 256 bytes at a time in a
+      // padded 32 x 272-byte area (4 bf16 or 2 fp32 fragments per pass), then
+      // store 4 full 256-byte rows per instruction (16 bytes per lane) instead
+      // of short pieces of 32 rows.
+      if (y_st && (tm + 1) * BM <= g.m && (tn + 1) * BN <= g.n) {
+        constexpr int PITCH = 272;
+        constexpr int ESZ = BF16OUT ? 2 : 4;
+        constexpr int FPP = 256 / (32 * ESZ);   // fragments per pass
+        const int lslot = cbuf == 0 ? NBUF - 1 : cbuf - 1;
+        uint8_t* tb = lds + lslot * STAGE_BYTES + wave * (32 * PITCH);
+        __builtin_amdgcn_s_barrier();   // every wave is done reading that slot
+#pragma unroll
+        for (int bb = 0; bb < FM; ++bb) {
+#pragma unroll
+          for (int a0 = 0; a0 < FN; a0 += FPP) {
+#pragma unroll
+            for (int a = a0; a < a0 + FPP; ++a)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                uint8_t* dst = tb + lr * PITCH + ((a - a0) * 32 + 8 * t + 4 * lg) * ESZ;
+                if constexpr (BF16OUT) {
+                  *reinterpret_cast<uint2*>(dst) =
+                      make_uint2(pack_bf16(acc[a][bb][4 * t], acc[a][bb][4 * t + 1]),
+                                 pack_bf16(acc[a][bb][4 * t + 2], acc[a][bb][4 * t + 3]));
+                } else {
+                  *reinterpret_cast<float4*>(dst) = make_float4(acc[a][bb][4 * t], acc[a][bb][4 * t + 1],
+                                                                acc[a][bb][4 * t + 2], acc[a][bb][4 * t + 3]);
+                }
+              }
+            // the area is private to this wave: its LDS writes land before its reads
+            const int m0 = tm * BM + wm * (BM / WM) + 32 * bb;
+            const int64_t n0 = tn * BN + wn * (BN / WN) + a0 * 32 + (lane & 15) * (16 / ESZ);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              const int row = 4 * r + (lane >> 4);
+              const uint4 v = *reinterpret_cast<const uint4*>(tb + row * PITCH + (lane & 15) * 16);
+              *reinterpret_cast<uint4*>(static_cast<uint8_t*>(g.y) + ((int64_t)(m0 + row) * g.ld_y + n0) * ESZ) = v;
+            }
+          }
+        }
+        continue;
+      }
+    }
 #pragma unroll
     for (int bb = 0; bb < FM; ++bb) {
       const int m = tm * BM + wm * (BM / WM) + 32 * bb + lr;
