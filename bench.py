@@ -239,7 +239,7 @@ def main():
     q_gbps = q_bytes / (q_us * 1e-6) / 1e9
     y_bytes = m * n * (2 if wl.out_dtype == "bf16" else 4)
     g_bytes = (m + n) * (k // 2 + k // 32) + y_bytes
-    traffic = recorded_traffic("gemm", args.workload, source_digest("gemm.hip", "internal.h"))
+    traffic = recorded_traffic("gemm", args.workload, source_digest("gemm.hip", "gemm_large.hip", "internal.h"))
     q_traffic = recorded_traffic("quantize", args.workload, source_digest("quantize.hip", "internal.h"))
 
     out = {
