@@ -11,15 +11,18 @@ codes, scales, Y) that the working set exceeds the 256 MB Infinity Cache.
 
 Prints one JSON line:
   value       2*M*N*K / (time of one quantize + GEMM step), TFLOP/s
-  roofline    the GEMM kernel (the dominant kernel): algorithmic FLOPs per
-              launch / its mean launch time from HIP events recorded around
-              every launch in the timed region, against the dense MXFP4 MFMA
-              peak; `traffic` = HBM bytes per launch from rocprofv3 counters
-              (profiles/), or null if the kernel source changed since
+  roofline    the GEMM kernel (the dominant kernel), timed by HIP events
+              recorded around every launch in the timed region.  Large M: the
+              MFMA-bound large-tile kernel, algorithmic FLOPs per launch / its
+              mean launch time, against the dense MXFP4 MFMA peak.  M <= 64
+              (decode): the HBM-bound small-M kernel, algorithmic bytes (both
+              operands' codes and scales read once, Y written) / launch time,
+              against HBM.  `traffic` = HBM bytes per launch from rocprofv3
+              counters (profiles/), or null if the kernel source changed since
   quantize    the quantizer kernel: algorithmic bytes (X read, codes and
               scales written) per launch / its mean launch time, against HBM
   copy_gbps   a plain device copy in the same run (practical HBM ceiling)
-  cpu_baseline  the CPU oracle on a bounded row sample of the same workload
+  cpu_baseline  the CPU oracle on the same workload (all rows by default)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -239,11 +242,25 @@ def main():
     q_gbps = q_bytes / (q_us * 1e-6) / 1e9
     y_bytes = m * n * (2 if wl.out_dtype == "bf16" else 4)
     g_bytes = (m + n) * (k // 2 + k // 32) + y_bytes
-    traffic = recorded_traffic("gemm", args.workload, source_digest("gemm.hip", "gemm_large.hip", "internal.h"))
+    small_m = m <= 64        # decode shapes run the small-M kernel, bound by streaming W from HBM
+    g_src = ("gemm.hip", "gemm_small.hip", "internal.h") if small_m else ("gemm.hip", "gemm_large.hip", "internal.h")
+    traffic = recorded_traffic("gemm", args.workload, source_digest(*g_src))
     q_traffic = recorded_traffic("quantize", args.workload, source_digest("quantize.hip", "internal.h"))
+    if small_m:
+        g_gbps = g_bytes / (g_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(g_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(g_gbps / PEAK_HBM_GBPS, 4), "kernel": "gemm_small"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_MXFP4_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_MXFP4_TFLOPS, 4), "kernel": "gemm_large"}
+    roof.update({"traffic": traffic, "us_per_launch": round(g_us, 2),
+                 "us_min": round(float(np.min(g["g_ms"])) * 1e3, 2), "algorithmic_bytes": g_bytes,
+                 "algorithmic_flops": flops})
+    metric = METRIC if args.workload == "flux_up" else \
+        f"MXFP4 GEMM TFLOPS @ M={m},K={k},N={n} (% peak); quantize GB/s (% HBM)"
 
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -258,11 +275,7 @@ def main():
         "config": {"workload": args.workload, "m": m, "n": n, "k": k, "x_dtype": wl.x_dtype,
                    "rotation": wl.rot or "none", "out_dtype": wl.out_dtype, "layout": "tiled",
                    "buffer_sets": g["nsets"], "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_MXFP4_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_MXFP4_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "gemm", "us_per_launch": round(g_us, 2),
-                     "us_min": round(float(np.min(g["g_ms"])) * 1e3, 2),
-                     "algorithmic_bytes": g_bytes},
+        "roofline": roof,
         "quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": q_traffic, "us_per_launch": round(q_us, 2),

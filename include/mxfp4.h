@@ -55,8 +55,12 @@
  *    r * 64 + 16 * (c ^ ((r >> 1 ^ r >> 2) & 3)), with the row-major nibble
  *    order inside the block;
  *  - scales [T][S][256][4] bytes: the scale of block 4 s + c of row r at r * 4 + c.
- *  Rows rows .. 256 T - 1 are padding; the quantizer writes them as zero codes
- *  and zero scale bytes, and the GEMM never stores their results.  Every load
+ *  Rows rows .. 256 T - 1 are padding.  Their content is unspecified: each
+ *  output element of the GEMM depends on one real row of each operand only,
+ *  so padding never reaches a stored result, whatever it holds (NaN scale
+ *  bytes included).  The quantizer writes zero codes and scales into the
+ *  padding rows of the last 16-row group that holds real rows and leaves the
+ *  rest of the buffer untouched.  Every load
  *  the GEMM makes of a tiled operand is then a contiguous 1 KiB (codes) or
  *  256-byte (scales) run.  mxfp4_tiled_bytes gives the buffer sizes.
  *
@@ -135,7 +139,8 @@ typedef struct {
  *   rot     NULL or kind NONE: no rotation.
  *   layout  mxfp4_layout of the outputs.
  *   codes   device, 16-byte aligned (written): [rows][k/2] bytes (ROWMAJOR),
- *           or the tiled codes, padding rows included (TILED).
+ *           or the tiled codes, sized for the padding rows (TILED; see the
+ *           layout above for what is written there).
  *   scales  device (written): [rows][k/32] bytes (ROWMAJOR), or the tiled
  *           scales (TILED, 4-byte aligned).
  * Errors: INVALID_ARG for null pointers (when rows > 0), k % 32 != 0 (k % 128

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmxfp4.so")
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemm_large.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemm_large.hip", "gemm_small.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

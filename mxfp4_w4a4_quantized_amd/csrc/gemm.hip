@@ -255,6 +255,7 @@ hipError_t run(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.m == 0 || g.n == 0) return hipSuccess;
+  if (gemm_small_supported(g)) return launch_gemm_small(g, s);
   if (g.tiled) return gemm_large_supported(g) ? launch_gemm_large(g, s) : hipErrorInvalidValue;
   if (g.m > 64 && gemm_large_supported(g)) return launch_gemm_large(g, s);
   return run<128, 128, 64, 64>(g, s);

@@ -1,0 +1,276 @@
+// Small-M MXFP4 x MXFP4 GEMM for gfx950 (decode shapes: M <= 64 activation
+// rows against a large weight matrix).
+//
+// At decode sizes the layer is bound by reading the packed weights once from
+// HBM: N*K/2 code bytes plus N*K/32 scale bytes, against 2*M*N*K FLOPs
+// (arithmetic intensity ~ 3.8*M FLOP/B, far below the MFMA ridge).  The
+// kernel reads the MXFP4 operands directly, with no dequantize pass ("AMD
+// Quark delivers MXFP4 quantization for FLUX.1-dev on Instinct MI350 with
+// 1.92x speedup", "MXFP4 quantization for diffusion models"; the decode
+// setting is the LLM case of "Bridging the Gap Between Promise and
+// Performance for Microscaling FP4 Quantization", "GPU Kernel Ondersteuning
+// (QuTLASS)").
+//
+// MFMA: v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1.  Lane l
+// supplies row l % 16 of an operand and the 32-element block l / 16 of the
+// instruction's 128-element K step as 16 packed bytes, plus that block's
+// E8M0 byte (op_sel 0).  The result lane l holds D[4*(l/16) + r][l % 16].
+//
+// Design:
+//  * One workgroup per 16 * NG weight rows (W is the MFMA's first operand, so
+//    a lane ends with four consecutive output columns of one output row).  Its
+//    waves split K into contiguous step ranges; a final LDS reduction sums the
+//    waves' partial tiles.  NG = 2 (32 rows) while M <= 32: each activation
+//    fragment then feeds two weight fragments, which halves the activation
+//    reads from L2 -- at decode sizes those are as many bytes as the weights.
+//  * Every operand fragment is exactly one MX block, loaded straight into
+//    registers: 16 code bytes plus one scale byte per lane per K step.  A wave
+//    issues all the loads of a chunk of 8 steps before its first MFMA, so the
+//    whole weight matrix is in flight at once across the grid and the HBM
+//    stream never waits on arithmetic.  Weights are read with non-temporal
+//    loads (each byte is used once per call); the activation fragments are
+//    shared by every workgroup and stay in L2.
+//  * Row-major operands: a wave's code load covers 16 rows x 64 contiguous
+//    bytes.  Tiled operands: one K step of 16 rows is one contiguous 1 KiB
+//    run.  Rows beyond M or N are clamped to a valid row (their results are
+//    never stored); blocks beyond K are zero codes with a zero scale byte, so
+//    a K tail contributes exactly 0.
+//  * M is covered in groups of 16 rows that reuse the weight fragments held
+//    in registers.
+//  * A wave whose chunk of steps lies wholly inside K issues its loads with
+//    no predicates, so the waits before the MFMAs can count them down one by
+//    one; only a K tail takes the predicated path.
+#include "internal.h"
+
+namespace mxfp4 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 8;      // K steps (128 elements each) per register chunk
+constexpr int MAXW = 8;    // waves per workgroup (K split)
+constexpr int MAXMG = 4;   // 16-row M groups (M <= 64)
+constexpr int MAXACC = 4;  // NG * MG accumulator tiles per wave
+
+__device__ __forceinline__ int tiled_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+__device__ __forceinline__ v4f mma(const u32x4& a, const u32x4& b, const v4f& c, int sa, int sb) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 h = __builtin_convertvector(f2{a, b}, b2);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
+
+// Operand addressing for one lane: the fragment of K step s is 16 code bytes
+// at code + s * cstride and one scale byte at scale + s * sstride.
+struct Operand {
+  const uint8_t* code;
+  const uint8_t* scale;
+  int64_t cstride, sstride;
+};
+
+template <bool TILED>
+__device__ __forceinline__ Operand operand(const uint8_t* codes, const uint8_t* scales, int row,
+                                           int rows, int k, int lg) {
+  Operand o;
+  if constexpr (TILED) {
+    const int64_t nstage = k >> 7;
+    const int64_t t = row >> 8;
+    const int r = row & 255;
+    o.code = codes + t * nstage * 16384 + r * 64 + 16 * (lg ^ tiled_swz(r));
+    o.scale = scales + t * nstage * 1024 + r * 4 + lg;
+    o.cstride = 16384;
+    o.sstride = 1024;
+  } else {
+    const int64_t rr = row < rows ? row : rows - 1;
+    o.code = codes + rr * (k >> 1) + 16 * lg;
+    o.scale = scales + rr * (k >> 5) + lg;
+    o.cstride = 64;
+    o.sstride = 4;
+  }
+  return o;
+}
+
+template <int MG, int NG, bool BF16OUT, bool TILED>
+__global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int spw, int y_vec) {
+  static_assert(MG * NG <= MAXACC, "reduction buffer holds MAXACC tiles per wave");
+  __shared__ v4f red[MAXW][MAXACC][64];
+
+  const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NG;
+  const int kblocks = g.k >> 5;
+  const int nsteps = (g.k + 127) >> 7;
+  const int s_begin = wave * spw;
+  const int s_end = min(nsteps, s_begin + spw);
+
+  Operand w[NG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) w[q] = operand<TILED>(g.b_codes, g.b_scales, n0 + 16 * q + lr, g.n, g.k, lg);
+  Operand x[MG];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg) x[mg] = operand<TILED>(g.a_codes, g.a_scales, 16 * mg + lr, g.m, g.k, lg);
+
+  v4f acc[NG][MG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q)
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) acc[q][mg] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = s_begin; s0 < s_end; s0 += CH) {
+    // every step of the chunk inside this wave's range and inside K
+    const bool full = s0 + CH <= s_end && (TILED || 4 * (s0 + CH) <= kblocks);
+    u32x4 wf[NG][CH];
+    int ws[NG][CH];
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          wf[q][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[q].code + (s0 + j) * w[q].cstride));
+          ws[q][j] = w[q].scale[(s0 + j) * w[q].sstride];
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          const int s = s0 + j;
+          wf[q][j] = u32x4{0u, 0u, 0u, 0u};
+          ws[q][j] = 0;
+          if (s < s_end && (TILED || 4 * s + lg < kblocks)) {
+            wf[q][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[q].code + s * w[q].cstride));
+            ws[q][j] = w[q].scale[s * w[q].sstride];
+          }
+        }
+    }
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) {
+      u32x4 xf[CH];
+      int xs[CH];
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          xf[j] = *reinterpret_cast<const u32x4*>(x[mg].code + (s0 + j) * x[mg].cstride);
+          xs[j] = x[mg].scale[(s0 + j) * x[mg].sstride];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const int s = s0 + j;
+          xf[j] = u32x4{0u, 0u, 0u, 0u};
+          xs[j] = 0;
+          if (s < s_end && (TILED || 4 * s + lg < kblocks)) {
+            xf[j] = *reinterpret_cast<const u32x4*>(x[mg].code + s * x[mg].cstride);
+            xs[j] = x[mg].scale[s * x[mg].sstride];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        if (s0 + j < s_end) {
+#pragma unroll
+          for (int q = 0; q < NG; ++q) acc[q][mg] = mma(wf[q][j], xf[j], acc[q][mg], ws[q][j], xs[j]);
+        }
+    }
+  }
+
+  if (nwaves > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) red[wave][q * MG + mg][lane] = acc[q][mg];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    for (int w2 = 1; w2 < nwaves; ++w2) {
+#pragma unroll
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) acc[q][mg] += red[w2][q * MG + mg][lane];
+    }
+  }
+
+  // lane holds Y[16 mg + lr][n .. n + 3] of weight group q
+#pragma unroll
+  for (int q = 0; q < NG; ++q)
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) {
+      const int n = n0 + 16 * q + 4 * lg;
+      const int m = 16 * mg + lr;
+      if (m >= g.m) continue;
+      const v4f v = acc[q][mg];
+      if constexpr (BF16OUT) {
+        uint16_t* yp = static_cast<uint16_t*>(g.y) + (int64_t)m * g.ld_y + n;
+        if (y_vec && n + 3 < g.n) {
+          *reinterpret_cast<uint2*>(yp) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < g.n) yp[r] = (uint16_t)(pack_bf16(v[r], 0.f) & 0xFFFFu);
+        }
+      } else {
+        float* yp = static_cast<float*>(g.y) + (int64_t)m * g.ld_y + n;
+        if (y_vec && n + 3 < g.n) {
+          *reinterpret_cast<float4*>(yp) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < g.n) yp[r] = v[r];
+        }
+      }
+    }
+}
+
+template <int MG, int NG, bool BF16OUT, bool TILED>
+void launch(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s) {
+  const int grid = (g.n + 16 * NG - 1) / (16 * NG);
+  gemm_small_kernel<MG, NG, BF16OUT, TILED><<<grid, 64 * nwaves, 0, s>>>(g, spw, y_vec);
+}
+
+template <int MG, int NG>
+void launch_mg(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s) {
+  if (g.y_bf16) {
+    if (g.tiled) launch<MG, NG, true, true>(g, nwaves, spw, y_vec, s);
+    else launch<MG, NG, true, false>(g, nwaves, spw, y_vec, s);
+  } else {
+    if (g.tiled) launch<MG, NG, false, true>(g, nwaves, spw, y_vec, s);
+    else launch<MG, NG, false, false>(g, nwaves, spw, y_vec, s);
+  }
+}
+
+}  // namespace
+
+bool gemm_small_supported(const GemmArgs& g) { return g.m >= 1 && g.m <= 16 * MAXMG; }
+
+hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s) {
+  if (!gemm_small_supported(g)) return hipErrorInvalidValue;
+  const int nsteps = (g.k + 127) / 128;
+  int nwaves = (nsteps + CH - 1) / CH;
+  if (nwaves > MAXW) nwaves = MAXW;
+  if (nwaves < 1) nwaves = 1;
+  const int spw = (nsteps + nwaves - 1) / nwaves;
+  const size_t ybytes = g.y_bf16 ? 2 : 4;
+  const int y_vec = (((uintptr_t)g.y) % (4 * ybytes) == 0) && (g.ld_y % 4 == 0);
+  switch ((g.m + 15) / 16) {
+    case 1: launch_mg<1, 2>(g, nwaves, spw, y_vec, s); break;
+    case 2: launch_mg<2, 2>(g, nwaves, spw, y_vec, s); break;
+    case 3: launch_mg<3, 1>(g, nwaves, spw, y_vec, s); break;
+    default: launch_mg<4, 1>(g, nwaves, spw, y_vec, s); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mxfp4

@@ -46,4 +46,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 bool gemm_large_supported(const GemmArgs& a);
 hipError_t launch_gemm_large(const GemmArgs& a, hipStream_t s);
 
+// Small-M kernel (gemm_small.hip): 1 <= m <= 64, either layout; the kernel
+// for decode shapes, bound by streaming the weights from HBM.
+bool gemm_small_supported(const GemmArgs& a);
+hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t s);
+
 }  // namespace mxfp4

@@ -112,8 +112,9 @@ __device__ __forceinline__ int tiled_swz(int r) { return ((r >> 1) ^ (r >> 2)) &
 // Work split: every wave quantizes 64 blocks.  Row-major output: 64
 // consecutive blocks in row-major block order.  Tiled output: the 4 blocks of
 // one 128-element stage in 16 consecutive rows, so the wave's code stores are
-// one contiguous KiB of the tiled layout; padding rows load as zeros and
-// store zero codes and scales.
+// one contiguous KiB of the tiled layout.  Padding rows inside the last
+// 16-row group load as zeros and store zero codes and scales; the 16-row
+// groups past it are not written at all (no GEMM output depends on them).
 template <bool BF16, int ROT, int P, int Q>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int dense) {
   constexpr int CPB = BF16 ? 4 : 8;   // 16-byte chunks per 32-element block
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
   if (a.tiled) {
     rg = wid / nstage;
     st = wid - rg * nstage;
-    if (rg * 16 >= a.rows_pad) return;
+    if (rg * 16 >= a.rows) return;
   } else {
     wb0 = wid * 64;
     if (wb0 >= nblk) return;
@@ -240,7 +241,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
 
 template <bool BF16>
 hipError_t dispatch(const QuantArgs& a, hipStream_t s) {
-  const uint64_t blocks = (uint64_t)(a.tiled ? a.rows_pad : a.rows) * a.nblk_row;   // 64 per wave
+  const uint64_t rows = a.tiled ? (a.rows + 15) / 16 * 16 : a.rows;   // tiled: whole 16-row groups
+  const uint64_t blocks = rows * a.nblk_row;   // 64 per wave
   const dim3 grid((uint32_t)((blocks + kThreads - 1) / kThreads)), block(kThreads);
   const int dense = a.ld_x == (int64_t)a.nblk_row * 32;
   if (a.rot == 0) {

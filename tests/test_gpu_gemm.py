@@ -153,6 +153,77 @@ def test_tiled_operands(m, n, k):
     assert np.array_equal(y16.view(torch.int16).cpu().numpy().view(np.uint16), bf16_rne(y32))
 
 
+# Shapes for the small-M kernel (M <= 64): every number of 16-row M groups,
+# N not a multiple of 16 or of 4, K tails inside the last 128-element step,
+# one to eight waves splitting K, and waves that loop over several register
+# chunks of K steps.
+SMALL_M_SHAPES = [
+    (1, 14336, 4096), (7, 3, 32), (16, 2000, 4128), (33, 517, 12288), (48, 64, 160),
+    (64, 130, 1024), (20, 4100, 20000), (2, 77, 96)]
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_M_SHAPES)
+def test_small_m_shapes(m, n, k):
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    ac, as_ = workloads.random_mxfp4(rng, m, k)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+    check_full(ac, as_, bc, bs, "small-m")
+
+
+SMALL_M_TILED = [(1, 300, 128), (33, 1000, 12288), (64, 256, 384), (50, 4097, 1024), (16, 14336, 4096)]
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_M_TILED)
+def test_small_m_tiled(m, n, k):
+    test_tiled_operands(m, n, k)
+
+
+def test_small_m_strided_output():
+    rng = np.random.default_rng(81)
+    m, n, k = 10, 90, 256
+    ac, as_ = workloads.random_mxfp4(rng, m, k)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+    ref = oracle.gemm(ac, as_, bc, bs)
+    for dt, off, fill in ((torch.float32, 4, 7.0), (torch.float32, 5, 7.0), (torch.bfloat16, 4, 3.0),
+                          (torch.bfloat16, 5, 3.0)):
+        big = torch.full((m, n + 12), fill, dtype=dt, device=DEV)
+        y = big[:, off:off + n]
+        announce("gemm small strided", m, n, k, dt, off)
+        mx.gemm(*map(to_dev, (ac, as_, bc, bs)), dt, y=y)
+        torch.cuda.synchronize()
+        if dt == torch.float32:
+            err = norm_err(y.cpu().numpy(), ref, row_norms(ac, as_), row_norms(bc, bs))
+            assert err <= TOL
+        host = big.float().cpu().numpy()
+        assert (host[:, :off] == fill).all() and (host[:, off + n:] == fill).all()   # no stray writes
+
+
+@pytest.mark.parametrize("m,n,k", [(20, 300, 256), (40, 70, 384), (300, 520, 256)])
+def test_tiled_padding_is_ignored(m, n, k):
+    """Padding rows of tiled operands hold garbage (code bytes 0xFF = -6, scale
+    bytes 0xFF = NaN): no stored output may depend on them (small-M and
+    large-tile kernels)."""
+    rng = np.random.default_rng(m + n + k)
+    ac, as_ = workloads.random_mxfp4(rng, m, k)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+
+    def padded(c, s):
+        rp = mx.padded_rows(c.shape[0])
+        pc = np.full((rp, c.shape[1]), 0xFF, np.uint8)
+        ps = np.full((rp, s.shape[1]), 0xFF, np.uint8)
+        pc[:c.shape[0]], ps[:s.shape[0]] = c, s
+        return mx.tile_host(pc, ps)
+
+    announce("gemm tiled padding garbage", m, n, k)
+    dev = [to_dev(t) for t in (*padded(ac, as_), *padded(bc, bs))]
+    y32 = mx.gemm(*dev, torch.float32, layout=mx.TILED, m=m, n=n)
+    torch.cuda.synchronize()
+    got = y32.cpu().numpy()
+    assert np.isfinite(got).all()
+    ref = oracle.gemm(ac, as_, bc, bs)
+    assert norm_err(got, ref, row_norms(ac, as_), row_norms(bc, bs)) <= TOL
+
+
 def test_extreme_scales():
     # scale bytes near both ends of the E8M0 range (products stay finite)
     rng = np.random.default_rng(77)

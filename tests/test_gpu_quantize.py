@@ -148,23 +148,28 @@ def test_strided_input_rows():
     (1024, 3072, True, "h32"), (16, 4096, True, "kron")])
 def test_tiled_layout_matches_oracle(rows, k, bf16, rot):
     """Tiled output (the GEMM-native layout): untiled on the host it must equal
-    the oracle's codes and scales bit for bit, and the padding rows must be
-    zero."""
+    the oracle's codes and scales bit for bit.  The padding rows of the last
+    16-row group holding real rows are written as zeros; the padding rows past
+    it are left untouched (here: the 0xFF the buffers were filled with)."""
     rng = np.random.default_rng(rows * 3 + k)
     x = workloads.random_blocks(rng, rows, k)
     if bf16:
         x = workloads.bf16_bits(x)
     r = rand_kron(4, 8, 9) if rot == "kron" else rot
     announce("quantize tiled", rows, k, "bf16" if bf16 else "f32", rot)
-    c, s = mx.quantize_rotate(dev_x(x, bf16), r, layout=mx.TILED)
+    rp = mx.padded_rows(rows)
+    c = torch.full((rp, k // 2), 0xFF, dtype=torch.uint8, device=DEV)
+    s = torch.full((rp, k // 32), 0xFF, dtype=torch.uint8, device=DEV)
+    mx.quantize_rotate(dev_x(x, bf16), r, codes=c, scales=s, layout=mx.TILED)
     torch.cuda.synchronize()
     tc, ts = c.cpu().numpy(), s.cpu().numpy()
-    assert tc.shape == (mx.padded_rows(rows), k // 2)
     got = mx.untile_host(tc, ts, rows)
     ref = oracle.quantize(x, rot=oracle_rot(r), bf16=bf16)
     assert_same(got, ref, f"tiled {rows}x{k}")
-    pc, ps = mx.untile_host(tc, ts, mx.padded_rows(rows))
-    assert not pc[rows:].any() and not ps[rows:].any()
+    pc, ps = mx.untile_host(tc, ts, rp)
+    r16 = (rows + 15) // 16 * 16
+    assert not pc[rows:r16].any() and not ps[rows:r16].any()
+    assert (pc[r16:] == 0xFF).all() and (ps[r16:] == 0xFF).all()
 
 
 def test_tiled_strided_input():
