@@ -10,8 +10,13 @@ before the timed region; the step cycles through enough buffer sets (X, W,
 codes, scales, Y) that the working set exceeds the 256 MB Infinity Cache.
 
 Prints one JSON line:
-  value       2*M*N*K / (time of one quantize + GEMM step), TFLOP/s
-  roofline    the GEMM kernel (the dominant kernel), timed by HIP events
+  value       2*M*N*K / (time of one step), TFLOP/s.  A step is one quantize +
+              GEMM.  For decode shapes (M <= 64, bf16 activations) both that
+              and one launch of the fused layer (mxfp4_linear_small) are
+              timed; the faster is the step (config.path) and the other is
+              reported beside it (`split` or `fused`)
+  roofline    the dominant kernel (the GEMM, or the fused layer for decode
+              shapes, bytes = bf16 X + MXFP4 W + Y), timed by HIP events
               recorded around every launch in the timed region.  Large M: the
               MFMA-bound large-tile kernel, algorithmic FLOPs per launch / its
               mean launch time, against the dense MXFP4 MFMA peak.  M <= 64
@@ -120,35 +125,45 @@ def gpu_leg(name: str, steps: int, warmup: int):
     log(f"workload {name}: M={m} N={n} K={k} rot={wl.rot} x={wl.x_dtype} y={wl.out_dtype}; "
         f"{nsets} buffer sets of {set_bytes / 2**20:.1f} MiB")
 
-    def step(s):
-        mx.quantize_rotate(s["x"], rot, s["xc"], s["xs"], layout=lay)
-        mx.gemm(s["xc"], s["xs"], s["wc"], s["ws"], out_dtype, s["y"], layout=lay)
-
-    for i in range(warmup):
-        step(sets[i % nsets])
-    torch.cuda.synchronize()
+    split = [lambda s: mx.quantize_rotate(s["x"], rot, s["xc"], s["xs"], layout=lay),
+             lambda s: mx.gemm(s["xc"], s["xs"], s["wc"], s["ws"], out_dtype, s["y"], layout=lay)]
+    # decode shapes: the fused layer (activation quantization inside the GEMM, one launch)
+    use_fused = (m <= mx.LINEAR_SMALL_MAX_M and bf16_in and (wl.rot != "kron" or 2 <= wl.p <= 16))
+    fused = [lambda s: mx.linear_small(s["x"], s["wc"], s["ws"], rot, out_dtype, s["y"], layout=lay, n=n)]
 
     stream = torch.cuda.current_stream(dev)   # the stream every launch goes to
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(steps):
-        s = sets[i % nsets]
-        e = ev[i]
-        e[0].record(stream)
-        mx.quantize_rotate(s["x"], rot, s["xc"], s["xs"], layout=lay)
-        e[1].record(stream)
-        mx.gemm(s["xc"], s["xs"], s["wc"], s["ws"], out_dtype, s["y"], layout=lay)
-        e[2].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
-    q_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    g_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+
+    def time_loop(parts):
+        """Time `steps` steps; HIP events on the launch stream around every
+        part of every step, and around the whole loop."""
+        for i in range(warmup):
+            for f in parts:
+                f(sets[i % nsets])
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for i in range(steps):
+            s = sets[i % nsets]
+            e = ev[i]
+            e[0].record(stream)
+            for j, f in enumerate(parts):
+                f(s)
+                e[j + 1].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per = [np.array([e[j].elapsed_time(e[j + 1]) for e in ev]) for j in range(len(parts))]
+        return t0.elapsed_time(t1), wall, per
+
+    total_ms, wall, (q_ms, g_ms) = time_loop(split)
+    fused_res = None
+    if use_fused:
+        f_total, f_wall, (f_ms,) = time_loop(fused)
+        fused_res = dict(total_ms=f_total, wall_s=f_wall, ms=f_ms)
 
     # plain device copy of 1 GiB: the practical HBM ceiling in this run
     nb = 1 << 30
@@ -170,7 +185,7 @@ def gpu_leg(name: str, steps: int, warmup: int):
 
     props = torch.cuda.get_device_properties(dev)
     return dict(m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms,
-                copy_gbps=copy_gbps, nsets=nsets, device=props.name,
+                fused=fused_res, copy_gbps=copy_gbps, nsets=nsets, device=props.name,
                 cus=props.multi_processor_count, arch=getattr(props, "gcnArchName", ""))
 
 
@@ -256,6 +271,29 @@ def main():
     roof.update({"traffic": traffic, "us_per_launch": round(g_us, 2),
                  "us_min": round(float(np.min(g["g_ms"])) * 1e3, 2), "algorithmic_bytes": g_bytes,
                  "algorithmic_flops": flops})
+    split_info = {"ms_per_step": round(ms_step, 5), "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2)}
+    fz = g["fused"]
+    if fz is not None and fz["total_ms"] > g["total_ms"]:
+        # the two-launch path was faster for this workload: it is the step, the fused figures are reported
+        split_info = None
+        fused_only = {"ms_per_step": round(fz["total_ms"] / args.steps, 5),
+                      "us_per_launch": round(float(np.mean(fz["ms"])) * 1e3, 2)}
+        fz = None
+    else:
+        fused_only = None
+    if fz is not None:
+        # the step is the fused layer: one launch reads bf16 X and the MXFP4 weights, writes Y
+        ms_step = fz["total_ms"] / args.steps
+        f_us = float(np.mean(fz["ms"])) * 1e3
+        f_bytes = x_bytes + n * (k // 2 + k // 32) + y_bytes
+        f_gbps = f_bytes / (f_us * 1e-6) / 1e9
+        f_traffic = recorded_traffic("linear_small", args.workload,
+                                     source_digest("gemm_small.hip", "block_quant.h", "internal.h"))
+        split_info["gemm_roofline"] = roof
+        roof = {"bound": "hbm", "achieved": round(f_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(f_gbps / PEAK_HBM_GBPS, 4), "kernel": "linear_small", "traffic": f_traffic,
+                "us_per_launch": round(f_us, 2), "us_min": round(float(np.min(fz["ms"])) * 1e3, 2),
+                "algorithmic_bytes": f_bytes, "algorithmic_flops": flops}
     metric = METRIC if args.workload == "flux_up" else \
         f"MXFP4 GEMM TFLOPS @ M={m},K={k},N={n} (% peak); quantize GB/s (% HBM)"
 
@@ -274,6 +312,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "m": m, "n": n, "k": k, "x_dtype": wl.x_dtype,
                    "rotation": wl.rot or "none", "out_dtype": wl.out_dtype, "layout": "tiled",
+                   "path": "fused" if fz is not None else "quantize+gemm",
                    "buffer_sets": g["nsets"], "parallelism": "single-gpu"},
         "roofline": roof,
         "quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
@@ -281,6 +320,8 @@ def main():
                      "traffic": q_traffic, "us_per_launch": round(q_us, 2),
                      "us_min": round(float(np.min(g["q_ms"])) * 1e3, 2),
                      "algorithmic_bytes": q_bytes},
+        "split": split_info if fz is not None else None,
+        "fused": fused_only,
         "copy_gbps": round(g["copy_gbps"], 1),
         "device": {"name": g["device"], "arch": g["arch"], "cus": g["cus"]},
     }

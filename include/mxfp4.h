@@ -172,6 +172,31 @@ MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
                                   int64_t k, int32_t layout, void* y, int32_t y_dtype, int64_t ld_y,
                                   void* stream);
 
+/* Fused small-M linear layer Y = Q(rot(X)) * W^T for decode shapes: the
+ * activations are rotated and quantized inside the GEMM, each block straight
+ * into the matrix-core operand registers, so the quantized activations never
+ * reach memory and the layer is one launch.  The rotation "fused into the
+ * quantization and matmul kernels" is the design of "Bridging the Gap Between
+ * Promise and Performance for Microscaling FP4 Quantization", "GPU Kernel
+ * Ondersteuning (QuTLASS)"; the quantization rule is the one above, so Y
+ * equals mxfp4_quantize_rotate followed by mxfp4_gemm.
+ *   x       device, [m][ld_x] BF16 activations, 16-byte aligned, ld_x a
+ *           multiple of 8, ld_x >= k.
+ *   rot     NULL / NONE, HADAMARD32, or KRON with 2 <= p <= 16.
+ *   w_codes/w_scales  device, W (n rows, pre-quantized) in `layout`.
+ *   m       1 <= m <= 64 (0 is a no-op); n >= 0; k > 0 multiple of 32 (of
+ *           128 for TILED).
+ *   y       device, [m][ld_y] of y_dtype (F32 or BF16), ld_y >= n.
+ * Errors: INVALID_ARG as for mxfp4_quantize_rotate and mxfp4_gemm;
+ *   UNSUPPORTED for m > 64, F32 activations, a KRON rotation with p = 1 or
+ *   p = 32, or misaligned pointers (use mxfp4_quantize_rotate + mxfp4_gemm
+ *   there); HIP if the launch fails. */
+MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_t m, int64_t k,
+                                          int64_t ld_x, const mxfp4_rotation* rot,
+                                          const uint8_t* w_codes, const uint8_t* w_scales, int64_t n,
+                                          int32_t layout, void* y, int32_t y_dtype, int64_t ld_y,
+                                          void* stream);
+
 /* Buffer sizes of a TILED operand with `rows` rows and `k` columns (k > 0, a
  * multiple of 128; rows >= 0): *codes_bytes = 256 T * k / 2 and
  * *scales_bytes = 256 T * k / 32 with T = ceil(rows / 256).

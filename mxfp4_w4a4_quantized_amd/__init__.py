@@ -45,8 +45,9 @@ TILE_ROWS, TILE_K = 256, 128
 
 HADAMARD32 = "h32"
 
-EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_gemm", "mxfp4_tiled_bytes", "mxfp4_inverse_transpose",
-            "mxfp4_status_string", "mxfp4_abi_version")
+EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_gemm", "mxfp4_linear_small", "mxfp4_tiled_bytes",
+            "mxfp4_inverse_transpose", "mxfp4_status_string", "mxfp4_abi_version")
+LINEAR_SMALL_MAX_M = 64
 
 
 class Mxfp4Error(RuntimeError):
@@ -77,6 +78,9 @@ def lib() -> ctypes.CDLL:
     L.mxfp4_quantize_rotate.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), i32, vp, vp, vp]
     L.mxfp4_gemm.restype = i32
     L.mxfp4_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, i32, vp, i32, i64, vp]
+    L.mxfp4_linear_small.restype = i32
+    L.mxfp4_linear_small.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), vp, vp, i64, i32,
+                                     vp, i32, i64, vp]
     L.mxfp4_tiled_bytes.restype = i32
     L.mxfp4_tiled_bytes.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.mxfp4_inverse_transpose.restype = i32
@@ -226,6 +230,37 @@ def linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, rot=N
     pre-quantized weights (in the same layout; n = weight rows for TILED)."""
     a_codes, a_scales = quantize_rotate(x, rot, layout=layout)
     return gemm(a_codes, a_scales, w_codes, w_scales, out_dtype, y, layout=layout, m=x.shape[0], n=n)
+
+
+def linear_small(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, rot=None,
+                 out_dtype=torch.bfloat16, y: torch.Tensor = None, layout: int = ROWMAJOR,
+                 n: int = None) -> torch.Tensor:
+    """Fused small-M linear layer (decode): bf16 x [m, k] with 1 <= m <= 64 is
+    rotated and quantized inside the GEMM (one launch, no quantized
+    activations in memory); same result as linear()."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    m, k = x.shape
+    if n is None:
+        n = w_codes.shape[0]
+    cshape, sshape = _out_shapes(n, k, layout)
+    if tuple(w_codes.shape) != cshape or tuple(w_scales.shape) != sshape:
+        raise ValueError(f"weights: codes/scales must be {cshape} / {sshape}")
+    for t in (w_codes, w_scales):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("codes and scales must be contiguous uint8 tensors")
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    if y.dim() != 2 or tuple(y.shape) != (m, n) or y.stride(1) != 1:
+        raise ValueError("y must be [m, n] with unit column stride")
+    desc, _keep = _rot_desc(rot, x.device)
+    st = lib().mxfp4_linear_small(
+        x.data_ptr(), _dtype_code(x.dtype), m, k, x.stride(0),
+        ctypes.byref(desc) if desc is not None else None,
+        w_codes.data_ptr(), w_scales.data_ptr(), n, layout,
+        y.data_ptr(), _dtype_code(y.dtype), y.stride(0), _stream(x.device))
+    _check(st, "mxfp4_linear_small")
+    return y
 
 
 def quantize_weight(w: torch.Tensor, rot=None, layout: int = ROWMAJOR):

@@ -15,6 +15,31 @@ mxfp4_status from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 
+struct Rot {
+  int32_t kind = MXFP4_ROT_NONE, p = 0, q = 0;
+  const float* fa = nullptr;
+  const float* fb = nullptr;
+};
+
+// Validates a rotation descriptor (NULL = none).
+mxfp4_status parse_rotation(const mxfp4_rotation* rot, Rot& r) {
+  if (rot == nullptr) return MXFP4_OK;
+  r.kind = rot->kind;
+  if (r.kind != MXFP4_ROT_NONE && r.kind != MXFP4_ROT_HADAMARD32 && r.kind != MXFP4_ROT_KRON)
+    return MXFP4_ERR_INVALID_ARG;
+  if (rot->reserved != 0) return MXFP4_ERR_INVALID_ARG;
+  if (r.kind == MXFP4_ROT_KRON) {
+    r.p = rot->p;
+    r.q = rot->q;
+    if (r.p < 1 || r.q < 1 || r.p * r.q != 32 || (r.p & (r.p - 1)) != 0) return MXFP4_ERR_INVALID_ARG;
+    if (rot->a == nullptr || rot->b == nullptr) return MXFP4_ERR_INVALID_ARG;
+    r.fa = rot->a;
+    r.fb = rot->b;
+    if (!aligned(r.fa, 4) || !aligned(r.fb, 4)) return MXFP4_ERR_UNSUPPORTED;
+  }
+  return MXFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -49,23 +74,9 @@ MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype, int
   if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
   const bool tiled = layout == MXFP4_LAYOUT_TILED;
   if (rows < 0 || k <= 0 || (k % (tiled ? mxfp4::kTileK : 32)) != 0 || ld_x < k) return MXFP4_ERR_INVALID_ARG;
-  int32_t kind = MXFP4_ROT_NONE, p = 0, q = 0;
-  const float *fa = nullptr, *fb = nullptr;
-  if (rot != nullptr) {
-    kind = rot->kind;
-    if (kind != MXFP4_ROT_NONE && kind != MXFP4_ROT_HADAMARD32 && kind != MXFP4_ROT_KRON)
-      return MXFP4_ERR_INVALID_ARG;
-    if (rot->reserved != 0) return MXFP4_ERR_INVALID_ARG;
-    if (kind == MXFP4_ROT_KRON) {
-      p = rot->p;
-      q = rot->q;
-      if (p < 1 || q < 1 || p * q != 32 || (p & (p - 1)) != 0) return MXFP4_ERR_INVALID_ARG;
-      if (rot->a == nullptr || rot->b == nullptr) return MXFP4_ERR_INVALID_ARG;
-      fa = rot->a;
-      fb = rot->b;
-      if (!aligned(fa, 4) || !aligned(fb, 4)) return MXFP4_ERR_UNSUPPORTED;
-    }
-  }
+  Rot r;
+  const mxfp4_status rs = parse_rotation(rot, r);
+  if (rs != MXFP4_OK) return rs;
   if (rows == 0) return MXFP4_OK;
   if (x == nullptr || codes == nullptr || scales == nullptr) return MXFP4_ERR_INVALID_ARG;
   const int64_t elem = (x_dtype == MXFP4_BF16) ? 2 : 4;
@@ -79,11 +90,11 @@ MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype, int
   a.ld_x = ld_x;
   a.rows = static_cast<uint32_t>(rows);
   a.nblk_row = static_cast<uint32_t>(k / 32);
-  a.rot = kind;
-  a.p = p;
-  a.q = q;
-  a.fa = fa;
-  a.fb = fb;
+  a.rot = r.kind;
+  a.p = r.p;
+  a.q = r.q;
+  a.fa = r.fa;
+  a.fb = r.fb;
   a.codes = codes;
   a.scales = scales;
   a.tiled = tiled;
@@ -122,6 +133,52 @@ MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
   g.y_bf16 = (y_dtype == MXFP4_BF16);
   g.tiled = tiled;
   return from_hip(mxfp4::launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t ld_x,
+                                          const mxfp4_rotation* rot, const uint8_t* w_codes,
+                                          const uint8_t* w_scales, int64_t n, int32_t layout, void* y,
+                                          int32_t y_dtype, int64_t ld_y, void* stream) {
+  if (x_dtype != MXFP4_F32 && x_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
+  if (y_dtype != MXFP4_F32 && y_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
+  if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
+  const bool tiled = layout == MXFP4_LAYOUT_TILED;
+  if (m < 0 || n < 0 || k <= 0 || (k % (tiled ? mxfp4::kTileK : 32)) != 0 || ld_x < k || ld_y < n)
+    return MXFP4_ERR_INVALID_ARG;
+  Rot r;
+  const mxfp4_status rs = parse_rotation(rot, r);
+  if (rs != MXFP4_OK) return rs;
+  if (m == 0 || n == 0) return MXFP4_OK;
+  if (x == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr) return MXFP4_ERR_INVALID_ARG;
+  if (m > 64 || x_dtype != MXFP4_BF16) return MXFP4_ERR_UNSUPPORTED;
+  if (r.kind == MXFP4_ROT_KRON && (r.p < 2 || r.p > 16)) return MXFP4_ERR_UNSUPPORTED;
+  if (n >= kMaxDim || k >= kMaxDim || ld_x >= kMaxDim) return MXFP4_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || ((ld_x * 2) % 16) != 0 || !aligned(w_codes, 16)) return MXFP4_ERR_UNSUPPORTED;
+  if (tiled && !aligned(w_scales, 4)) return MXFP4_ERR_UNSUPPORTED;
+  const int64_t ybytes = (y_dtype == MXFP4_BF16) ? 2 : 4;
+  if (!aligned(y, ybytes)) return MXFP4_ERR_UNSUPPORTED;
+
+  mxfp4::LinearArgs L;
+  L.x = x;
+  L.ld_x = ld_x;
+  L.x_bf16 = true;
+  L.rot = r.kind;
+  L.p = r.p;
+  L.q = r.q;
+  L.fa = r.fa;
+  L.fb = r.fb;
+  L.g.a_codes = nullptr;
+  L.g.a_scales = nullptr;
+  L.g.b_codes = w_codes;
+  L.g.b_scales = w_scales;
+  L.g.m = static_cast<int32_t>(m);
+  L.g.n = static_cast<int32_t>(n);
+  L.g.k = static_cast<int32_t>(k);
+  L.g.y = y;
+  L.g.ld_y = ld_y;
+  L.g.y_bf16 = (y_dtype == MXFP4_BF16);
+  L.g.tiled = tiled;
+  return from_hip(mxfp4::launch_linear_small(L, static_cast<hipStream_t>(stream)));
 }
 
 // Binary64 Gauss-Jordan elimination with partial pivoting on [M | I]; the

@@ -41,6 +41,7 @@
 //    no predicates, so the waits before the MFMAs can count them down one by
 //    one; only a K tail takes the predicated path.
 #include "internal.h"
+#include "block_quant.h"
 
 namespace mxfp4 {
 namespace {
@@ -71,6 +72,29 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return u;
 }
 
+// Store Y[m][n .. n + 3] (bounds-checked against N) in the output dtype.
+__device__ __forceinline__ void store4(const GemmArgs& g, int m, int n, const v4f& v, int y_vec) {
+  if (g.y_bf16) {
+    uint16_t* yp = static_cast<uint16_t*>(g.y) + (int64_t)m * g.ld_y + n;
+    if (y_vec && n + 3 < g.n) {
+      *reinterpret_cast<uint2*>(yp) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < g.n) yp[r] = (uint16_t)(pack_bf16(v[r], 0.f) & 0xFFFFu);
+    }
+  } else {
+    float* yp = static_cast<float*>(g.y) + (int64_t)m * g.ld_y + n;
+    if (y_vec && n + 3 < g.n) {
+      *reinterpret_cast<float4*>(yp) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < g.n) yp[r] = v[r];
+    }
+  }
+}
+
 // Operand addressing for one lane: the fragment of K step s is 16 code bytes
 // at code + s * cstride and one scale byte at scale + s * sstride.
 struct Operand {
@@ -99,6 +123,12 @@ __device__ __forceinline__ Operand operand(const uint8_t* codes, const uint8_t* 
     o.sstride = 4;
   }
   return o;
+}
+
+// Operand addressing with the layout chosen at run time (fused kernel).
+__device__ __forceinline__ Operand operand_rt(bool tiled, const uint8_t* codes, const uint8_t* scales, int row,
+                                              int rows, int k, int lg) {
+  return tiled ? operand<true>(codes, scales, row, rows, k, lg) : operand<false>(codes, scales, row, rows, k, lg);
 }
 
 template <int MG, int NG, bool BF16OUT, bool TILED>
@@ -251,9 +281,201 @@ void launch_mg(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s)
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Fused small-M linear layer: Y = Q(rot(X)) * W^T with the activation
+// quantization done inside the GEMM.  Lane (r, g) of a wave needs, for K step
+// s, the MX block 4 s + g of activation row r as its MFMA operand; it loads
+// those 32 elements itself, rotates and quantizes them with the quantizer's
+// own arithmetic (block_quant.h, so the codes equal the quantizer's bit for
+// bit) and feeds the codes and scale byte straight to the MFMA: quantized
+// activations never touch memory and there is no second launch.
+//
+// Per chunk of KC steps a wave issues its activation loads (L2-resident: every
+// workgroup reads the same rows) before its weight loads, so it can rotate and
+// quantize while the weights stream in from HBM.  NG weight groups of 16 rows
+// per workgroup (32 rows for M <= 32) keep the redundant per-workgroup
+// quantization to N / (16 NG) copies; KC = 4 steps per wave keeps the
+// registers within two waves per SIMD.  Activations are bf16; the rotation is
+// none, Hadamard-32 or a Kronecker product with 2 <= P <= 16 (the factors sit
+// in scalar registers; the degenerate 1 x 32 and 32 x 1 forms, a dense 32 x 32
+// factor, are left to the separate quantizer).
+constexpr int KC = 4;          // K steps per fused chunk
+
+template <bool XBF16>
+struct RawBlock {
+  u32x4 c[XBF16 ? 4 : 8];
+};
+
+template <bool XBF16>
+__device__ __forceinline__ void load_block(const uint8_t* p, bool ok, RawBlock<XBF16>& b) {
+#pragma unroll
+  for (int i = 0; i < (XBF16 ? 4 : 8); ++i)
+    b.c[i] = ok ? *reinterpret_cast<const u32x4*>(p + 16 * i) : u32x4{0u, 0u, 0u, 0u};
+}
+
+template <bool XBF16, int ROT, int P, int Q>
+__device__ __forceinline__ void quantize_raw(const RawBlock<XBF16>& b, const float* fa, const float* fb, u32x4& codes,
+                                             int& sbyte) {
+  float v[32];
+  if constexpr (XBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = blockq::bf16_lo(b.c[i][j]);
+        v[8 * i + 2 * j + 1] = blockq::bf16_hi(b.c[i][j]);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * i + j] = __uint_as_float(b.c[i][j]);
+  }
+  blockq::rotate_block<ROT, P, Q>(fa, fb, v);
+  uint32_t w[4];
+  sbyte = (int)blockq::encode_block(v, w);
+  codes = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <int MG, int NG, bool XBF16, int ROT, int P, int Q>
+__global__ __launch_bounds__(64 * MAXW) void linear_small_kernel(LinearArgs L, int spw, int y_vec) {
+  static_assert(MG * NG <= MAXACC, "reduction buffer holds MAXACC tiles per wave");
+  __shared__ v4f red[MAXW][MAXACC][64];
+  const GemmArgs& g = L.g;
+
+  const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NG;
+  const int kblocks = g.k >> 5;
+  const int nsteps = (g.k + 127) >> 7;
+  const int s_begin = wave * spw;
+  const int s_end = min(nsteps, s_begin + spw);
+  const int64_t esz = XBF16 ? 2 : 4;
+  const uint8_t* xb = static_cast<const uint8_t*>(L.x);
+
+  Operand w[NG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) w[q] = operand_rt(g.tiled, g.b_codes, g.b_scales, n0 + 16 * q + lr, g.n, g.k, lg);
+  // activation row of this lane in M group mg (rows past M quantize zeros)
+  const uint8_t* xrow[MG];
+  bool xin[MG];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg) {
+    const int row = 16 * mg + lr;
+    xin[mg] = row < g.m;
+    xrow[mg] = xb + (int64_t)(xin[mg] ? row : 0) * L.ld_x * esz;
+  }
+
+  v4f acc[NG][MG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q)
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) acc[q][mg] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = s_begin; s0 < s_end; s0 += KC) {
+    u32x4 wf[NG][KC];
+    int ws[NG][KC];
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) {
+      // activation loads of this M group first: they do not wait behind the
+      // weight loads issued next
+      RawBlock<XBF16> raw[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const int s = s0 + j, col = 4 * s + lg;
+        const bool ok = s < s_end && col < kblocks && xin[mg];
+        load_block<XBF16>(xrow[mg] + (int64_t)col * 32 * esz, ok, raw[j]);
+      }
+      if (mg == 0) {
+#pragma unroll
+        for (int j = 0; j < KC; ++j)
+#pragma unroll
+          for (int q = 0; q < NG; ++q) {
+            const int s = s0 + j;
+            wf[q][j] = u32x4{0u, 0u, 0u, 0u};
+            ws[q][j] = 0;
+            if (s < s_end && (g.tiled || 4 * s + lg < kblocks)) {
+              wf[q][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[q].code + s * w[q].cstride));
+              ws[q][j] = w[q].scale[s * w[q].sstride];
+            }
+          }
+      }
+      u32x4 xf[KC];
+      int xs[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) quantize_raw<XBF16, ROT, P, Q>(raw[j], L.fa, L.fb, xf[j], xs[j]);
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        if (s0 + j < s_end) {
+#pragma unroll
+          for (int q = 0; q < NG; ++q) acc[q][mg] = mma(wf[q][j], xf[j], acc[q][mg], ws[q][j], xs[j]);
+        }
+    }
+  }
+
+  if (nwaves > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) red[wave][q * MG + mg][lane] = acc[q][mg];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    for (int w2 = 1; w2 < nwaves; ++w2) {
+#pragma unroll
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) acc[q][mg] += red[w2][q * MG + mg][lane];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NG; ++q)
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) {
+      const int n = n0 + 16 * q + 4 * lg;
+      const int m = 16 * mg + lr;
+      if (m >= g.m) continue;
+      store4(g, m, n, acc[q][mg], y_vec);
+    }
+}
+
+template <int MG, int NG, bool XBF16, int ROT, int P, int Q>
+void launch_fused(const LinearArgs& L, int nwaves, int spw, int y_vec, hipStream_t s) {
+  const int grid = (L.g.n + 16 * NG - 1) / (16 * NG);
+  linear_small_kernel<MG, NG, XBF16, ROT, P, Q><<<grid, 64 * nwaves, 0, s>>>(L, spw, y_vec);
+}
+
+template <int MG, int NG, bool XBF16>
+hipError_t launch_fused_rot(const LinearArgs& L, int nwaves, int spw, int y_vec, hipStream_t s) {
+  if (L.rot == 0) launch_fused<MG, NG, XBF16, 0, 1, 32>(L, nwaves, spw, y_vec, s);
+  else if (L.rot == 1) launch_fused<MG, NG, XBF16, 1, 1, 32>(L, nwaves, spw, y_vec, s);
+  else {
+    switch (L.p) {
+      case 2: launch_fused<MG, NG, XBF16, 2, 2, 16>(L, nwaves, spw, y_vec, s); break;
+      case 4: launch_fused<MG, NG, XBF16, 2, 4, 8>(L, nwaves, spw, y_vec, s); break;
+      case 8: launch_fused<MG, NG, XBF16, 2, 8, 4>(L, nwaves, spw, y_vec, s); break;
+      case 16: launch_fused<MG, NG, XBF16, 2, 16, 2>(L, nwaves, spw, y_vec, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipSuccess;
+}
+
+template <int MG, int NG>
+hipError_t launch_fused_mg(const LinearArgs& L, int nwaves, int spw, int y_vec, hipStream_t s) {
+  return launch_fused_rot<MG, NG, true>(L, nwaves, spw, y_vec, s);
+}
+
 }  // namespace
 
 bool gemm_small_supported(const GemmArgs& g) { return g.m >= 1 && g.m <= 16 * MAXMG; }
+
+bool linear_small_supported(const LinearArgs& L) {
+  return gemm_small_supported(L.g) && L.x_bf16 && (L.rot != 2 || (L.p >= 2 && L.p <= 16));
+}
 
 hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s) {
   if (!gemm_small_supported(g)) return hipErrorInvalidValue;
@@ -270,6 +492,30 @@ hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s) {
     case 3: launch_mg<3, 1>(g, nwaves, spw, y_vec, s); break;
     default: launch_mg<4, 1>(g, nwaves, spw, y_vec, s); break;
   }
+  return hipGetLastError();
+}
+
+}  // namespace mxfp4
+
+namespace mxfp4 {
+
+hipError_t launch_linear_small(const LinearArgs& L, hipStream_t s) {
+  if (!linear_small_supported(L)) return hipErrorInvalidValue;
+  const int nsteps = (L.g.k + 127) / 128;
+  int nwaves = (nsteps + KC - 1) / KC;
+  if (nwaves > MAXW) nwaves = MAXW;
+  if (nwaves < 1) nwaves = 1;
+  const int spw = (nsteps + nwaves - 1) / nwaves;
+  const size_t ybytes = L.g.y_bf16 ? 2 : 4;
+  const int y_vec = (((uintptr_t)L.g.y) % (4 * ybytes) == 0) && (L.g.ld_y % 4 == 0);
+  hipError_t e;
+  switch ((L.g.m + 15) / 16) {
+    case 1: e = launch_fused_mg<1, 4>(L, nwaves, spw, y_vec, s); break;
+    case 2: e = launch_fused_mg<2, 2>(L, nwaves, spw, y_vec, s); break;
+    case 3: e = launch_fused_mg<3, 1>(L, nwaves, spw, y_vec, s); break;
+    default: e = launch_fused_mg<4, 1>(L, nwaves, spw, y_vec, s); break;
+  }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

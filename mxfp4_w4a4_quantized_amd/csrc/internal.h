@@ -51,4 +51,21 @@ hipError_t launch_gemm_large(const GemmArgs& a, hipStream_t s);
 bool gemm_small_supported(const GemmArgs& a);
 hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t s);
 
+// Fused small-M linear layer (gemm_small.hip): the activations are rotated
+// and quantized inside the GEMM, lane by lane, straight into the MFMA
+// operands (1 <= m <= 64; W in either layout, described by g.b_* / g.tiled;
+// g.a_* unused).
+struct LinearArgs {
+  const void* x;       // [m][ld_x] fp32 or bf16
+  int64_t ld_x;        // elements
+  bool x_bf16;
+  int32_t rot;         // mxfp4_rot_kind
+  int32_t p, q;
+  const float* fa;
+  const float* fb;
+  GemmArgs g;
+};
+bool linear_small_supported(const LinearArgs& a);
+hipError_t launch_linear_small(const LinearArgs& a, hipStream_t s);
+
 }  // namespace mxfp4

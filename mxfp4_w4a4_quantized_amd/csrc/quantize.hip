@@ -30,69 +30,17 @@
 // library is compiled with -ffp-contract=off and the only fused operations
 // are explicit fmaf calls), so codes and scales are reproducible bit for bit.
 #include "internal.h"
+#include "block_quant.h"
 
 namespace mxfp4 {
 namespace {
+
+using namespace blockq;
 
 constexpr int kThreads = 256;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Normalized Hadamard-32 (Sylvester order) as five butterfly stages with
-// strides 1, 2, 4, 8, 16, then one multiply by fp32(1/sqrt(32)).
-__device__ __forceinline__ void hadamard32(float (&v)[32]) {
-#pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 32; i += 2 * h) {
-#pragma unroll
-      for (int j = i; j < i + h; ++j) {
-        const float u = v[j], w = v[j + h];
-        v[j] = u + w;
-        v[j + h] = u - w;
-      }
-    }
-  }
-  const float c = __uint_as_float(0x3E3504F3u);  // nearest fp32 to 1/sqrt(32)
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = v[i] * c;
-}
-
-// y = (A (x) B) x on the block seen as the P x Q matrix Xm[j][l] = x[Q*j+l]:
-// stage 1 U[j][k] = chain_l B[k][l] Xm[j][l], stage 2 y[Q*i+k] =
-// chain_j A[i][j] U[j][k]; each chain is the rounded first product followed
-// by fused multiply-adds in ascending order.  The factor loads are uniform
-// across the wave and become scalar loads.
-template <int P, int Q>
-__device__ __forceinline__ void kron32(const float* __restrict__ fa, const float* __restrict__ fb,
-                                       float (&v)[32]) {
-  static_assert(P * Q == 32, "P*Q must be 32");
-  float u[32];
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-#pragma unroll
-    for (int k = 0; k < Q; ++k) {
-      float acc = fb[k * Q] * v[Q * j];
-#pragma unroll
-      for (int l = 1; l < Q; ++l) acc = __builtin_fmaf(fb[k * Q + l], v[Q * j + l], acc);
-      u[j * Q + k] = acc;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-#pragma unroll
-    for (int k = 0; k < Q; ++k) {
-      float acc = fa[i * P] * u[k];
-#pragma unroll
-      for (int j = 1; j < P; ++j) acc = __builtin_fmaf(fa[i * P + j], u[j * Q + k], acc);
-      v[Q * i + k] = acc;
-    }
-  }
-}
 
 // Chunk swizzle inside the LDS slab: a block is CPB 16-byte chunks; the
 // 16 lanes of one ds_read_b128 phase read chunk q of 16 consecutive blocks,
@@ -197,34 +145,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
       for (int j = 0; j < 4; ++j) v[4 * i + j] = __uint_as_float(q4[i][j]);
   }
 
-  if constexpr (ROT == 1) hadamard32(v);
-  if constexpr (ROT == 2) kron32<P, Q>(a.fa, a.fb, v);
-
-  // block amax (exact)
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-
-  // E8M0: floor(log2 amax) - 2 clamped at -127 is the biased exponent field
-  // of amax minus 2 (subnormal and zero amax have field 0 and clamp).
-  const uint32_t ef = __float_as_uint(amax) >> 23;
-  const uint32_t sbyte = ef > 2u ? ef - 2u : 0u;
-  // The block scale 2^e as fp32 (2^-127 is the subnormal 0x00400000).  The
-  // converter divides by its scale operand exactly -- it equals converting
-  // v * 2^-e with scale 1 for every finite input, checked on the device for
-  // all bf16 values and e in [-127, 125] -- so no separate multiply is needed.
-  const float scale = __uint_as_float(sbyte ? sbyte << 23 : 0x00400000u);
-
+  rotate_block<ROT, P, Q>(a.fa, a.fb, v);
   uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t acc = 0;
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 0], v[8 * i + 1], scale, 0);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 2], v[8 * i + 3], scale, 1);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 4], v[8 * i + 5], scale, 2);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 6], v[8 * i + 7], scale, 3);
-    w[i] = acc;
-  }
+  const uint32_t sbyte = encode_block(v, w);
   if (a.tiled) {
     const uint32_t t = orow / kTileRows, r = orow % kTileRows, sg = ocol / 4, cb = ocol % 4;
     const uint64_t ts = (uint64_t)t * nstage + sg;   // (tile, stage) index

@@ -109,6 +109,40 @@ def test_gemm_argument_errors():
     assert g(A, A, 1 << 30, A, A, 4, 64, R, A, 0, 4, None) == UNS
 
 
+def ls(*args):
+    return mx.lib().mxfp4_linear_small(*args)
+
+
+def test_linear_small_argument_errors():
+    """Synchronous validation of the fused small-M linear entry point (no
+    device access happens on any of these paths)."""
+    INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
+    A, R, T, BF, F = ALIGNED, mx.ROWMAJOR, mx.TILED, mx.MXFP4_BF16, mx.MXFP4_F32
+    assert ls(A, 7, 4, 64, 64, None, A, A, 8, R, A, F, 8, None) == INV    # bad x dtype
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, R, A, 9, 8, None) == INV   # bad y dtype
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, 2, A, F, 8, None) == INV   # bad layout
+    assert ls(A, BF, 4, 48, 64, None, A, A, 8, R, A, F, 8, None) == INV   # k % 32
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, T, A, F, 8, None) == INV   # tiled: k % 128
+    assert ls(A, BF, 4, 64, 32, None, A, A, 8, R, A, F, 8, None) == INV   # ld_x < k
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, R, A, F, 4, None) == INV   # ld_y < n
+    assert ls(A, BF, -1, 64, 64, None, A, A, 8, R, A, F, 8, None) == INV  # m < 0
+    assert ls(NULL, BF, 4, 64, 64, None, A, A, 8, R, A, F, 8, None) == INV
+    assert ls(A, BF, 4, 64, 64, None, NULL, A, 8, R, A, F, 8, None) == INV
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, R, NULL, F, 8, None) == INV
+    assert ls(NULL, BF, 0, 64, 64, None, NULL, NULL, 8, R, NULL, F, 8, None) == OK   # m == 0
+    assert ls(A, BF, 65, 64, 64, None, A, A, 8, R, A, F, 8, None) == UNS  # m > 64
+    assert ls(A, F, 4, 64, 64, None, A, A, 8, R, A, F, 8, None) == UNS    # fp32 activations
+    assert ls(MISALIGNED, BF, 4, 64, 64, None, A, A, 8, R, A, F, 8, None) == UNS
+    assert ls(A, BF, 4, 64, 68, None, A, A, 8, R, A, F, 8, None) == UNS   # row stride not 16 B
+    assert ls(A, BF, 4, 64, 64, None, A + 8, A, 8, R, A, F, 8, None) == UNS
+    assert ls(A, BF, 4, 128, 128, None, A, A + 2, 8, T, A, F, 8, None) == UNS   # tiled scales
+    for p_, q_ in ((1, 32), (32, 1)):
+        kr = mx.RotationDesc(mx.ROT_KRON, p_, q_, 0, A, A)
+        assert ls(A, BF, 4, 64, 64, ctypes.byref(kr), A, A, 8, R, A, F, 8, None) == UNS
+    kr = mx.RotationDesc(mx.ROT_KRON, 4, 4, 0, A, A)
+    assert ls(A, BF, 4, 64, 64, ctypes.byref(kr), A, A, 8, R, A, F, 8, None) == INV   # p*q != 32
+
+
 def test_tiled_bytes():
     INV = mx.MXFP4_ERR_INVALID_ARG
     assert mx.tiled_bytes(1, 128) == (256 * 64, 256 * 4)

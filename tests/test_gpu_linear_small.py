@@ -1,0 +1,181 @@
+"""GPU parity of the fused small-M linear layer (mxfp4_linear_small): the
+activations are rotated and quantized inside the GEMM.
+
+Two kinds of check:
+  * Exact pin of the in-GEMM quantization.  With W the K x K identity
+    (quantized without rotation: each row has one element 1.0, encoded exactly
+    as code 4.0 at scale 2^-2), every output element is a single exact product,
+    Y[m][j] = x_hat[m][j].  So the fused kernel's fp32 output must equal the
+    dequantized oracle codes of rot(X) bit for bit.
+  * The layer against the oracle's binary64 GEMM of the oracle-quantized
+    activations, at the normalized 1e-5 bound of the GEMM tests, for random
+    MXFP4 weights; bf16 output equal to the round-to-nearest-even bf16 of the
+    same kernel's fp32 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_w4a4_quantized_amd as mx
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 1e-5
+LAYOUTS = {"rowmajor": mx.ROWMAJOR, "tiled": mx.TILED}
+
+
+def announce(*what):
+    print("[case]", *what, flush=True)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bf16_dev(x_bits):
+    return to_dev(x_bits.view(np.int16)).view(torch.bfloat16)
+
+
+def make_rot(r, seed=5):
+    if r is None or r == "h32":
+        return r
+    p, q = r
+    rng = np.random.default_rng(seed)
+    a = (np.eye(p) + 0.1 * rng.standard_normal((p, p))).astype(np.float32)
+    b = (np.eye(q) + 0.1 * rng.standard_normal((q, q))).astype(np.float32)
+    return mx.Kron.from_host(a, b, DEV)
+
+
+def oracle_rot(rot):
+    if rot is None or rot == "h32":
+        return rot
+    return ("kron", rot.a.cpu().numpy(), rot.b.cpu().numpy())
+
+
+def weights_dev(wc, ws, layout):
+    if layout == mx.TILED:
+        wc, ws = mx.tile_host(wc, ws)
+    return to_dev(wc), to_dev(ws)
+
+
+def row_norms(codes, scales):
+    return np.sqrt((oracle.dequantize(codes, scales) ** 2).sum(axis=1))
+
+
+def norm_err(got, ref, na, nb):
+    den = np.outer(na, nb)
+    diff = np.abs(got.astype(np.float64) - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(den > 0, diff / den, np.where(diff == 0, 0.0, np.inf))
+    return float(rel.max()) if rel.size else 0.0
+
+
+ROTS = [None, "h32", (2, 16), (4, 8), (8, 4), (16, 2)]
+
+
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("m", [1, 16, 33, 64])
+@pytest.mark.parametrize("rot", ROTS, ids=str)
+def test_fused_quantization_is_bit_exact(rot, m, layout):
+    k = 512
+    rng = np.random.default_rng(m * 7 + k)
+    x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
+    r = make_rot(rot)
+    xc, xs = oracle.quantize(x, rot=oracle_rot(r), bf16=True)
+    want = oracle.dequantize(xc, xs)                       # exact in binary64 and in fp32
+    wc, ws = oracle.quantize(np.eye(k, dtype=np.float32))  # identity weights, no rotation
+    assert np.array_equal(oracle.dequantize(wc, ws), np.eye(k))
+    announce("linear_small identity", rot, m, k, layout)
+    lay = LAYOUTS[layout]
+    dwc, dws = weights_dev(wc, ws, lay)
+    y = mx.linear_small(bf16_dev(x), dwc, dws, r, torch.float32, layout=lay, n=k)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    bad = np.count_nonzero(got != want)
+    assert bad == 0, f"{bad} of {got.size} dequantized activations differ"
+
+
+SHAPES = [
+    (1, 300, 4096, "rowmajor"), (16, 1000, 4128, "rowmajor"), (7, 77, 96, "rowmajor"),
+    (17, 513, 1024, "tiled"), (40, 256, 12288, "tiled"), (64, 130, 384, "rowmajor"),
+    (16, 14336, 4096, "tiled"), (33, 70, 2048, "tiled")]
+
+
+@pytest.mark.parametrize("rot", [None, "h32", (4, 8)], ids=str)
+@pytest.mark.parametrize("m,n,k,layout", SHAPES)
+def test_fused_linear_matches_oracle(m, n, k, layout, rot):
+    rng = np.random.default_rng(m + 3 * n + k)
+    x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
+    wc, ws = workloads.random_mxfp4(rng, n, k)
+    r = make_rot(rot)
+    lay = LAYOUTS[layout]
+    announce("linear_small", m, n, k, layout, rot)
+    dwc, dws = weights_dev(wc, ws, lay)
+    xd = bf16_dev(x)
+    y32 = mx.linear_small(xd, dwc, dws, r, torch.float32, layout=lay, n=n)
+    y16 = mx.linear_small(xd, dwc, dws, r, torch.bfloat16, layout=lay, n=n)
+    torch.cuda.synchronize()
+    xc, xs = oracle.quantize(x, rot=oracle_rot(r), bf16=True)
+    ref = oracle.gemm(xc, xs, wc, ws)
+    err = norm_err(y32.cpu().numpy(), ref, row_norms(xc, xs), row_norms(wc, ws))
+    assert err <= TOL, f"normalized error {err:.3e}"
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+
+
+def test_fused_strided_input_and_output():
+    rng = np.random.default_rng(91)
+    m, n, k = 12, 90, 256
+    full = workloads.bf16_bits(workloads.random_blocks(rng, m, 640))
+    x = bf16_dev(full)[:, :k]                                   # ld_x = 640 > k
+    wc, ws = workloads.random_mxfp4(rng, n, k)
+    xc, xs = oracle.quantize(np.ascontiguousarray(full[:, :k]), rot="h32", bf16=True)
+    ref = oracle.gemm(xc, xs, wc, ws)
+    for dt, off, fill in ((torch.float32, 4, 7.0), (torch.float32, 5, 7.0), (torch.bfloat16, 5, 3.0)):
+        big = torch.full((m, n + 12), fill, dtype=dt, device=DEV)
+        y = big[:, off:off + n]
+        announce("linear_small strided", m, n, k, dt, off)
+        mx.linear_small(x, to_dev(wc), to_dev(ws), "h32", dt, y=y)
+        torch.cuda.synchronize()
+        if dt == torch.float32:
+            assert norm_err(y.cpu().numpy(), ref, row_norms(xc, xs), row_norms(wc, ws)) <= TOL
+        host = big.float().cpu().numpy()
+        assert (host[:, :off] == fill).all() and (host[:, off + n:] == fill).all()   # no stray writes
+
+
+def test_fused_decode_workload():
+    """The decode workload through the fused path: weights quantized on the
+    device with the weight side of the Kronecker transform (bit-exact against
+    the oracle), the layer against the oracle on every output element."""
+    inp = workloads.make("llm_decode_kron")
+    wl = inp["wl"]
+    rot = mx.Kron.from_host(inp["a"], inp["b"], DEV)
+    announce("linear_small workload", wl.name, wl.m, wl.n, wl.k)
+    wc, ws = mx.quantize_weight(to_dev(inp["w"]), rot, layout=mx.TILED)
+    y = mx.linear_small(bf16_dev(inp["x"]), wc, ws, rot, torch.float32, layout=mx.TILED, n=wl.n)
+    y_split = mx.linear(bf16_dev(inp["x"]), wc, ws, rot, torch.float32, layout=mx.TILED, n=wl.n)
+    torch.cuda.synchronize()
+    hwc, hws = mx.untile_host(wc.cpu().numpy(), ws.cpu().numpy(), wl.n)
+    wr = rot.weight_side()
+    rwc, rws = oracle.quantize(inp["w"], rot=("kron", wr.a.cpu().numpy(), wr.b.cpu().numpy()))
+    assert np.array_equal(hwc, rwc) and np.array_equal(hws, rws)
+    xc, xs = oracle.quantize(inp["x"], rot=("kron", inp["a"], inp["b"]), bf16=True)
+    ref = oracle.gemm(xc, xs, hwc, hws)
+    na, nb = row_norms(xc, xs), row_norms(hwc, hws)
+    err = norm_err(y.cpu().numpy(), ref, na, nb)
+    print(f"[result] fused decode: max normalized error {err:.3e}", flush=True)
+    assert err <= TOL
+    assert norm_err(y_split.cpu().numpy(), ref, na, nb) <= TOL
+
+
+def test_fused_unsupported_cases_raise():
+    x32 = torch.zeros((4, 64), dtype=torch.float32, device=DEV)
+    wc = torch.zeros((8, 32), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros((8, 2), dtype=torch.uint8, device=DEV)
+    with pytest.raises(mx.Mxfp4Error):
+        mx.linear_small(x32, wc, ws)                             # fp32 activations
+    x = torch.zeros((65, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(mx.Mxfp4Error):
+        mx.linear_small(x, wc, ws)                               # m > 64
