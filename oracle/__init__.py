@@ -23,6 +23,11 @@ What it computes (page titles and sections as the pages give them):
   * the GEMM on MXFP4 operands -- the Quark page, section "MXFP4 quantization
     for diffusion models" (no dequantization pass; output written as
     bf16/fp32).
+  * per-channel smoothing (the SmoothQuant baseline the KroQuant page compares
+    against): one fp32 multiply per element by a per-channel factor.
+  * MXFP4 scale fitting -- "Bridging the Gap ...", "Methodologie: MR-GPTQ"
+    item 2: the block exponent re-fitted among e0 - 1, e0, e0 + 1 by the
+    smallest binary64 squared error (the rule is a reading; see the C source).
 
 Every function is pinned by the ``-m "not gpu"`` tests (tests/test_oracle_*).
 """
@@ -35,7 +40,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle_mxfp4.so")
 _lib = None
 
-ROT_NONE, ROT_H32, ROT_KRON = 0, 1, 2
+ROT_NONE, ROT_H32, ROT_KRON, ROT_SMOOTH = 0, 1, 2, 3
 
 _f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
@@ -66,6 +71,10 @@ def _load():
         "oracle_inverse_transpose": (_int, [_f32p, _int, _f32p]),
         "oracle_quantize_f32": (_int, [_f32p, _i64, _i64, _i64, _int, _f32p, _int, _f32p, _int, _u8p, _u8p]),
         "oracle_quantize_bf16": (_int, [_u16p, _i64, _i64, _i64, _int, _f32p, _int, _f32p, _int, _u8p, _u8p]),
+        "oracle_quantize_f32_ex": (_int, [_f32p, _i64, _i64, _i64, _int, _f32p, _int, _f32p, _int, _int,
+                                          _u8p, _u8p]),
+        "oracle_quantize_bf16_ex": (_int, [_u16p, _i64, _i64, _i64, _int, _f32p, _int, _f32p, _int, _int,
+                                           _u8p, _u8p]),
         "oracle_rotate_f32": (_int, [_f32p, _i64, _i64, _int, _f32p, _int, _f32p, _int, _f32p]),
         "oracle_dequantize": (None, [_u8p, _u8p, _i64, _i64, _f64p]),
         "oracle_gemm_entries": (None, [_u8p, _u8p, _u8p, _u8p, _i64, _i64p, _i64p, _i64, _f64p]),
@@ -160,6 +169,9 @@ def _rot_args(rot):
         return ROT_NONE, dummy, 1, dummy, 1
     if rot == "h32":
         return ROT_H32, dummy, 1, dummy, 1
+    if rot[0] == "smooth":
+        r = np.ascontiguousarray(rot[1], dtype=np.float32).ravel()
+        return ROT_SMOOTH, r, 1, dummy, 1
     kind, a, b = rot
     assert kind == "kron"
     a = np.ascontiguousarray(a, dtype=np.float32)
@@ -171,6 +183,8 @@ def rotate(x: np.ndarray, rot) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     rows, k = x.shape
     kind, a, p, b, q = _rot_args(rot)
+    if kind == ROT_SMOOTH:
+        assert a.size == k
     y = np.empty_like(x)
     if _load().oracle_rotate_f32(x, rows, k, kind, a, p, b, q, y) != 0:
         raise ValueError("bad arguments")
@@ -179,20 +193,24 @@ def rotate(x: np.ndarray, rot) -> np.ndarray:
 
 # -------------------------------------------------------------- quantizer ---
 
-def quantize(x: np.ndarray, rot=None, bf16: bool = False):
+def quantize(x: np.ndarray, rot=None, bf16: bool = False, fit: bool = False):
     """Quantize rows of x to MXFP4.  x: float32 [rows, k], or uint16 bf16 bit
-    patterns [rows, k] with bf16=True.  Returns (codes [rows, k/2] uint8,
+    patterns [rows, k] with bf16=True.  rot: None, "h32", ("kron", A, B) or
+    ("smooth", r) with r the k per-channel factors.  fit: fitted block
+    exponents instead of the E8M0 rule.  Returns (codes [rows, k/2] uint8,
     scales [rows, k/32] uint8)."""
     rows, k = x.shape
     kind, a, p, b, q = _rot_args(rot)
+    if kind == ROT_SMOOTH:
+        assert a.size == k
     codes = np.empty((rows, k // 2), np.uint8)
     scales = np.empty((rows, k // 32), np.uint8)
     if bf16:
         x = np.ascontiguousarray(x, dtype=np.uint16)
-        rc = _load().oracle_quantize_bf16(x, rows, k, k, kind, a, p, b, q, codes, scales)
+        rc = _load().oracle_quantize_bf16_ex(x, rows, k, k, kind, a, p, b, q, int(fit), codes, scales)
     else:
         x = np.ascontiguousarray(x, dtype=np.float32)
-        rc = _load().oracle_quantize_f32(x, rows, k, k, kind, a, p, b, q, codes, scales)
+        rc = _load().oracle_quantize_f32_ex(x, rows, k, k, kind, a, p, b, q, int(fit), codes, scales)
     if rc != 0:
         raise ValueError("bad arguments")
     return codes, scales

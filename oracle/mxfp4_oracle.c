@@ -27,6 +27,11 @@
  *        "Tiefenanalyse" -- a learned Kronecker-structured invertible transform
  *        on each 32-element activation block; "Hintergrund" -- the inverse goes
  *        on the weights.
+ *  [P4s] same page, the comparison with SmoothQuant (per-channel scaling of the
+ *        activations, with the inverse scaling folded into the weights).
+ *  [P3f] "Bridging the Gap ...", "Methodologie: MR-GPTQ", item 2 -- for MXFP4
+ *        the exponent of the block scale is re-fitted ("scale fitting") to
+ *        match the grid to the data and lower the quantization error.
  *  [MX]  the OCP Microscaling Formats (MX) v1.0 specification that [P2] names:
  *        FP4 E2M1 element (bias 1, one mantissa bit, no Inf/NaN), E8M0 scale
  *        (value 2^(byte-127)), shared exponent floor(log2(amax)) - emax_elem
@@ -218,7 +223,7 @@ int oracle_inverse_transpose(const float* m, int n, float* out)
 /* Quantizer                                                                   */
 /* ------------------------------------------------------------------------- */
 
-enum { ROT_NONE = 0, ROT_H32 = 1, ROT_KRON = 2 };
+enum { ROT_NONE = 0, ROT_H32 = 1, ROT_KRON = 2, ROT_SMOOTH = 3 };
 
 /* bf16 -> fp32 widening is exact: the bf16 bits are the upper half. */
 static float widen_bf16(uint16_t h)
@@ -229,12 +234,38 @@ static float widen_bf16(uint16_t h)
     return f;
 }
 
-/* One 32-element block: optional rotation, block amax, E8M0 scale, E2M1
- * codes packed two per byte.
+/* Sum of squared errors of one block encoded with shared exponent e, in
+ * binary64: the sum runs over the elements in order, each term the exact
+ * difference v - x_hat squared (every step a single binary64 operation).
+ * READING ([P3f] names scale fitting without a formula): the fitted exponent
+ * is the one of e0 - 1, e0, e0 + 1 (e0 the rule of Q2) with the smallest
+ * such error; a candidate replaces the current best only when strictly
+ * smaller, tried in the order e0, e0 + 1, e0 - 1, so ties keep e0.  e0 - 1 is
+ * not tried at the lower clamp (e0 = -127); e0 + 1 <= 126 always holds for
+ * finite blocks. */
+static double block_sse(const float* v, int e)
+{
+    double s = 0.0;
+    int i;
+    for (i = 0; i < 32; ++i) {
+        int c = oracle_e2m1_encode(v[i], e);
+        double xh = oracle_e2m1_value(c) * ldexp(1.0, e);
+        double d = (double)v[i] - xh;
+        double d2 = d * d;
+        s = s + d2;
+    }
+    return s;
+}
+
+/* One 32-element block: optional rotation, block amax, E8M0 scale (the Q2
+ * rule, or the fitted exponent when fit != 0), E2M1 codes packed two per
+ * byte.  For ROT_SMOOTH, A points at this block's 32 per-channel factors.
  * READING (nibble order): element 2j goes to the low nibble of byte j and
- * element 2j+1 to the high nibble. */
+ * element 2j+1 to the high nibble.
+ * READING ([P4s]): the smoothing division by the per-channel factor s is one
+ * IEEE fp32 multiply by the caller's factor r = 1/s. */
 static void quantize_block(const float* xin, int rot, const float* A, int p,
-                           const float* B, int q, uint8_t* codes16,
+                           const float* B, int q, int fit, uint8_t* codes16,
                            uint8_t* scale)
 {
     float v[32];
@@ -242,13 +273,26 @@ static void quantize_block(const float* xin, int rot, const float* A, int p,
     int i, byte, e;
     if (rot == ROT_H32) oracle_fwht32(xin, v);
     else if (rot == ROT_KRON) oracle_kron_apply(A, p, B, q, xin, v);
-    else memcpy(v, xin, sizeof v);
+    else if (rot == ROT_SMOOTH) {
+        for (i = 0; i < 32; ++i) v[i] = xin[i] * A[i];
+    } else memcpy(v, xin, sizeof v);
     for (i = 0; i < 32; ++i) {
         float a = fabsf(v[i]);
         if (a > amax) amax = a;
     }
     byte = oracle_e8m0_from_amax(amax);
     e = byte - 127;
+    if (fit) {
+        double best = block_sse(v, e), err;
+        int e0 = e;
+        err = block_sse(v, e0 + 1);
+        if (err < best) { best = err; e = e0 + 1; }
+        if (e0 > -127) {
+            err = block_sse(v, e0 - 1);
+            if (err < best) { best = err; e = e0 - 1; }
+        }
+        byte = e + 127;
+    }
     for (i = 0; i < 16; ++i) {
         int lo = oracle_e2m1_encode(v[2 * i], e);
         int hi = oracle_e2m1_encode(v[2 * i + 1], e);
@@ -261,29 +305,31 @@ static int check_args(int64_t rows, int64_t k, int64_t ld, int rot, int p, int q
 {
     if (rows < 0 || k < 0 || (k % 32) != 0 || ld < k) return -1;
     if (rot == ROT_KRON && (p < 1 || q < 1 || p * q != 32)) return -1;
-    if (rot < ROT_NONE || rot > ROT_KRON) return -1;
+    if (rot < ROT_NONE || rot > ROT_SMOOTH) return -1;
     return 0;
 }
 
 /* Quantize a row-major fp32 matrix x[rows][ld] (first k columns).
- * codes: rows x k/2 bytes, scales: rows x k/32 bytes, both dense row-major. */
-int oracle_quantize_f32(const float* x, int64_t rows, int64_t k, int64_t ld,
-                        int rot, const float* A, int p, const float* B, int q,
-                        uint8_t* codes, uint8_t* scales)
+ * codes: rows x k/2 bytes, scales: rows x k/32 bytes, both dense row-major.
+ * ROT_SMOOTH: A holds k per-channel factors.  fit != 0: fitted exponents. */
+int oracle_quantize_f32_ex(const float* x, int64_t rows, int64_t k, int64_t ld,
+                           int rot, const float* A, int p, const float* B, int q,
+                           int fit, uint8_t* codes, uint8_t* scales)
 {
     int64_t r, b, nb = k / 32;
     if (check_args(rows, k, ld, rot, p, q)) return -1;
     for (r = 0; r < rows; ++r)
         for (b = 0; b < nb; ++b)
-            quantize_block(x + r * ld + 32 * b, rot, A, p, B, q,
+            quantize_block(x + r * ld + 32 * b, rot,
+                           rot == ROT_SMOOTH ? A + 32 * b : A, p, B, q, fit,
                            codes + r * (k / 2) + 16 * b, scales + r * nb + b);
     return 0;
 }
 
 /* Same for bf16 input (raw uint16 bit patterns), widened exactly to fp32. */
-int oracle_quantize_bf16(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
-                         int rot, const float* A, int p, const float* B, int q,
-                         uint8_t* codes, uint8_t* scales)
+int oracle_quantize_bf16_ex(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
+                            int rot, const float* A, int p, const float* B, int q,
+                            int fit, uint8_t* codes, uint8_t* scales)
 {
     int64_t r, b, nb = k / 32;
     float blk[32];
@@ -292,10 +338,24 @@ int oracle_quantize_bf16(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
     for (r = 0; r < rows; ++r)
         for (b = 0; b < nb; ++b) {
             for (i = 0; i < 32; ++i) blk[i] = widen_bf16(x[r * ld + 32 * b + i]);
-            quantize_block(blk, rot, A, p, B, q, codes + r * (k / 2) + 16 * b,
-                           scales + r * nb + b);
+            quantize_block(blk, rot, rot == ROT_SMOOTH ? A + 32 * b : A, p, B, q, fit,
+                           codes + r * (k / 2) + 16 * b, scales + r * nb + b);
         }
     return 0;
+}
+
+int oracle_quantize_f32(const float* x, int64_t rows, int64_t k, int64_t ld,
+                        int rot, const float* A, int p, const float* B, int q,
+                        uint8_t* codes, uint8_t* scales)
+{
+    return oracle_quantize_f32_ex(x, rows, k, ld, rot, A, p, B, q, 0, codes, scales);
+}
+
+int oracle_quantize_bf16(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
+                         int rot, const float* A, int p, const float* B, int q,
+                         uint8_t* codes, uint8_t* scales)
+{
+    return oracle_quantize_bf16_ex(x, rows, k, ld, rot, A, p, B, q, 0, codes, scales);
 }
 
 /* Rotation only (no quantization), for checking the rotation stage alone. */
@@ -310,7 +370,10 @@ int oracle_rotate_f32(const float* x, int64_t rows, int64_t k, int rot,
             float* d = y + r * k + 32 * b;
             if (rot == ROT_H32) oracle_fwht32(s, d);
             else if (rot == ROT_KRON) oracle_kron_apply(A, p, B, q, s, d);
-            else memcpy(d, s, 32 * sizeof(float));
+            else if (rot == ROT_SMOOTH) {
+                int i;
+                for (i = 0; i < 32; ++i) d[i] = s[i] * A[32 * b + i];
+            } else memcpy(d, s, 32 * sizeof(float));
         }
     return 0;
 }
