@@ -26,6 +26,12 @@ Prints one JSON line:
               counters (profiles/), or null if the kernel source changed since
   quantize    the quantizer kernel: algorithmic bytes (X read, codes and
               scales written) per launch / its mean launch time, against HBM
+  transforms  the quantizer on the same activations with each block transform
+              (none, Hadamard-32, Kronecker 4x8, per-channel smoothing), and
+              the step time with the same GEMM
+  weight_fit  offline weight quantization with the E8M0 rule and with fitted
+              block exponents: time, and the squared error of each against the
+              weight-side transformed fp32 weights
   copy_gbps   a plain device copy in the same run (practical HBM ceiling)
   cpu_baseline  the CPU oracle on the same workload (all rows by default)
 
@@ -80,6 +86,43 @@ def recorded_traffic(kernel: str, workload: str, digest: str):
     if not d or not t or d.group(1) != digest:
         return None
     return float(t.group(1))
+
+
+# ------------------------------------------------------ measurement helpers ---
+
+def _dequant(codes, scales):
+    """MXFP4 (row-major) -> fp32 on the device with torch ops (for error
+    figures only)."""
+    import torch
+    lut = torch.tensor([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6],
+                       dtype=torch.float32, device=codes.device)
+    c = torch.stack([codes & 15, codes >> 4], dim=-1).reshape(codes.shape[0], -1).long()
+    v = lut[c]
+    e = torch.exp2(scales.float() - 127).repeat_interleave(32, dim=1)
+    return v * e
+
+
+def _rotated(w, rot):
+    """Weights after the weight-side transform (fp32, for error figures)."""
+    import torch
+    import mxfp4_w4a4_quantized_amd as mx
+    if rot == "h32":
+        import math
+        blocks = w.reshape(w.shape[0], -1, 32).double()
+        h = torch.ones(1, 1, dtype=torch.float64, device=w.device)
+        for _ in range(5):
+            h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+        return (blocks @ h.T / math.sqrt(32)).reshape(w.shape).float()
+    if isinstance(rot, mx.Smooth):
+        return w * rot.r[None, :]
+    if isinstance(rot, mx.Kron):
+        t = torch.kron(rot.a.double(), rot.b.double())
+        return (w.reshape(w.shape[0], -1, 32).double() @ t.T).reshape(w.shape).float()
+    return w
+
+
+def _sse(codes, scales, ref):
+    return float(((_dequant(codes, scales).double() - ref.double()) ** 2).sum())
 
 
 # ----------------------------------------------------------------- GPU leg ---
@@ -165,6 +208,53 @@ def gpu_leg(name: str, steps: int, warmup: int):
         f_total, f_wall, (f_ms,) = time_loop(fused)
         fused_res = dict(total_ms=f_total, wall_s=f_wall, ms=f_ms)
 
+    # --- the transforms side by side on this workload's activations: the
+    # quantizer alone (the GEMM does not depend on the transform)
+    def time_parts(fn, reps=50):
+        for i in range(5):
+            fn(sets[i % nsets])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(sets[i % nsets])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    trng = np.random.default_rng(1)
+    tkinds = {"none": None, "h32": mx.HADAMARD32,
+              "kron4x8": mx.Kron.from_host((np.eye(4) + 0.1 * trng.standard_normal((4, 4))).astype(np.float32),
+                                           (np.eye(8) + 0.1 * trng.standard_normal((8, 8))).astype(np.float32), dev),
+              "smooth": mx.Smooth.from_host((0.5 + trng.random(k)).astype(np.float32), dev)}
+    transforms = {}
+    for tname, trot in tkinds.items():
+        tms = time_parts(lambda s_, r_=trot: mx.quantize_rotate(s_["x"], r_, s_["xc"], s_["xs"], layout=lay))
+        transforms[tname] = tms
+
+    # --- offline weight quantization: plain E8M0 rule vs fitted exponents, and
+    # the squared error of each against the (transformed) fp32 weights
+    w32 = torch.from_numpy(inp["w"]).to(dev)
+    wrot = rot.weight_side() if isinstance(rot, (mx.Kron, mx.Smooth)) else rot
+    wfit = {}
+    for fit in (False, True):
+        for _ in range(2):
+            wc_, ws_ = mx.quantize_rotate(w32, wrot, fit=fit)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            wc_, ws_ = mx.quantize_rotate(w32, wrot, fit=fit)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wfit["fit" if fit else "plain"] = dict(ms=e0.elapsed_time(e1) / 5, codes=wc_, scales=ws_)
+    wref = w32 if wrot is None else _rotated(w32, wrot)
+    for v in wfit.values():
+        v["sse"] = _sse(v.pop("codes"), v.pop("scales"), wref)
+    del w32, wref
+
     # plain device copy of 1 GiB: the practical HBM ceiling in this run
     nb = 1 << 30
     src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
@@ -185,7 +275,7 @@ def gpu_leg(name: str, steps: int, warmup: int):
 
     props = torch.cuda.get_device_properties(dev)
     return dict(m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms,
-                fused=fused_res, copy_gbps=copy_gbps, nsets=nsets, device=props.name,
+                fused=fused_res, copy_gbps=copy_gbps, transforms=transforms, wfit=wfit, nsets=nsets, device=props.name,
                 cus=props.multi_processor_count, arch=getattr(props, "gcnArchName", ""))
 
 
@@ -260,7 +350,7 @@ def main():
     small_m = m <= 64        # decode shapes run the small-M kernel, bound by streaming W from HBM
     g_src = ("gemm.hip", "gemm_small.hip", "internal.h") if small_m else ("gemm.hip", "gemm_large.hip", "internal.h")
     traffic = recorded_traffic("gemm", args.workload, source_digest(*g_src))
-    q_traffic = recorded_traffic("quantize", args.workload, source_digest("quantize.hip", "internal.h"))
+    q_traffic = recorded_traffic("quantize", args.workload, source_digest("quantize.hip", "block_quant.h", "internal.h"))
     if small_m:
         g_gbps = g_bytes / (g_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(g_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -322,6 +412,12 @@ def main():
                      "algorithmic_bytes": q_bytes},
         "split": split_info if fz is not None else None,
         "fused": fused_only,
+        "transforms": {t: {"quantize_us": round(v * 1e3, 2),
+                           "quantize_gbps": round(q_bytes / (v * 1e-3) / 1e9, 1),
+                           "step_us": round(v * 1e3 + g_us, 2)} for t, v in g["transforms"].items()},
+        "weight_fit": {"plain_ms": round(g["wfit"]["plain"]["ms"], 3), "fit_ms": round(g["wfit"]["fit"]["ms"], 3),
+                       "sse_plain": g["wfit"]["plain"]["sse"], "sse_fit": g["wfit"]["fit"]["sse"],
+                       "sse_ratio": round(g["wfit"]["fit"]["sse"] / max(g["wfit"]["plain"]["sse"], 1e-300), 4)},
         "copy_gbps": round(g["copy_gbps"], 1),
         "device": {"name": g["device"], "arch": g["arch"], "cus": g["cus"]},
     }

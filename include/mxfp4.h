@@ -100,11 +100,12 @@ typedef enum {
     MXFP4_BF16 = 1
 } mxfp4_dtype;
 
-/* Block rotation applied before quantization. */
+/* Block transform applied before quantization. */
 typedef enum {
     MXFP4_ROT_NONE = 0,        /* plain MXFP4 round-to-nearest */
     MXFP4_ROT_HADAMARD32 = 1,  /* y = H32 x / sqrt(32), Sylvester order */
-    MXFP4_ROT_KRON = 2         /* y = (A (x) B) x, A p x p, B q x q, p*q=32 */
+    MXFP4_ROT_KRON = 2,        /* y = (A (x) B) x, A p x p, B q x q, p*q=32 */
+    MXFP4_ROT_SMOOTH = 3       /* y[c] = x[c] * a[c], per-channel factors */
 } mxfp4_rot_kind;
 
 /* Memory layout of packed codes and scales (see "Packed layouts" above). */
@@ -120,13 +121,19 @@ typedef enum {
  * KRON evaluation order: with Xm[j][l] = x[q*j + l],
  *   U[j][k] = chain_l B[k][l] * Xm[j][l],  y[q*i + k] = chain_j A[i][j] * U[j][k],
  *   where a chain is the rounded first product followed by fused
- *   multiply-adds in ascending index order.  */
+ *   multiply-adds in ascending index order.
+ * SMOOTH: per-channel smoothing, the SmoothQuant-style baseline that
+ *   "KroQuant: ..." compares its transform with: column c of the input is
+ *   multiplied by a[c] (one fp32 multiply; a[c] = 1/s[c] divides by the
+ *   smoothing factor s[c], and the weights take a[c]^-1 = s[c]).  `a` holds
+ *   k factors, the k of the call.  Calibrating the factors is the caller's.  */
 typedef struct {
     int32_t kind;      /* mxfp4_rot_kind */
     int32_t p;         /* KRON: rows of A (1, 2, 4, 8, 16 or 32) */
     int32_t q;         /* KRON: rows of B, p * q == 32 */
     int32_t reserved;  /* must be 0 */
-    const float* a;    /* KRON: device pointer, p*p fp32 row-major */
+    const float* a;    /* KRON: device pointer, p*p fp32 row-major;
+                          SMOOTH: device pointer, k fp32 factors, 16-byte aligned */
     const float* b;    /* KRON: device pointer, q*q fp32 row-major */
 } mxfp4_rotation;
 
@@ -152,6 +159,21 @@ MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype,
                                              const mxfp4_rotation* rot, int32_t layout,
                                              uint8_t* codes, uint8_t* scales,
                                              void* stream);
+
+/* Scale-fitted quantization, for the offline weight side: as
+ * mxfp4_quantize_rotate, but each block's E8M0 exponent is the one of
+ * e0 - 1, e0, e0 + 1 (e0 the rule above) whose encoding has the smallest
+ * squared error against the transformed block -- each error summed in binary64
+ * over the 32 elements in order as s = s + (v - x_hat)^2, ties keeping e0,
+ * then e0 + 1 ("Bridging the Gap Between Promise and Performance for
+ * Microscaling FP4 Quantization", "Methodologie: MR-GPTQ" item 2 fits the
+ * MXFP4 scale exponent to the data; the candidate set and the error are this
+ * library's reading).  Same arguments and errors as mxfp4_quantize_rotate. */
+MXFP4_API mxfp4_status mxfp4_quantize_fit(const void* x, int32_t x_dtype,
+                                          int64_t rows, int64_t k, int64_t ld_x,
+                                          const mxfp4_rotation* rot, int32_t layout,
+                                          uint8_t* codes, uint8_t* scales,
+                                          void* stream);
 
 /* Y = A * B^T on MXFP4 operands, fp32 accumulation.
  *   a_codes/a_scales  device, A (m rows) in `layout`.
@@ -182,7 +204,7 @@ MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
  * equals mxfp4_quantize_rotate followed by mxfp4_gemm.
  *   x       device, [m][ld_x] BF16 activations, 16-byte aligned, ld_x a
  *           multiple of 8, ld_x >= k.
- *   rot     NULL / NONE, HADAMARD32, or KRON with 2 <= p <= 16.
+ *   rot     NULL / NONE, HADAMARD32, SMOOTH, or KRON with 2 <= p <= 16.
  *   w_codes/w_scales  device, W (n rows, pre-quantized) in `layout`.
  *   m       1 <= m <= 64 (0 is a no-op); n >= 0; k > 0 multiple of 32 (of
  *           128 for TILED).

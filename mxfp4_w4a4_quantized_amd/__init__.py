@@ -39,13 +39,13 @@ LIB_PATH = os.path.join(_HERE, "libmxfp4.so")
 
 MXFP4_OK, MXFP4_ERR_INVALID_ARG, MXFP4_ERR_UNSUPPORTED, MXFP4_ERR_HIP = 0, 1, 2, 3
 MXFP4_F32, MXFP4_BF16 = 0, 1
-ROT_NONE, ROT_HADAMARD32, ROT_KRON = 0, 1, 2
+ROT_NONE, ROT_HADAMARD32, ROT_KRON, ROT_SMOOTH = 0, 1, 2, 3
 ROWMAJOR, TILED = 0, 1
 TILE_ROWS, TILE_K = 256, 128
 
 HADAMARD32 = "h32"
 
-EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_gemm", "mxfp4_linear_small", "mxfp4_tiled_bytes",
+EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_quantize_fit", "mxfp4_gemm", "mxfp4_linear_small", "mxfp4_tiled_bytes",
             "mxfp4_inverse_transpose", "mxfp4_status_string", "mxfp4_abi_version")
 LINEAR_SMALL_MAX_M = 64
 
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.mxfp4_quantize_rotate.restype = i32
     L.mxfp4_quantize_rotate.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), i32, vp, vp, vp]
+    L.mxfp4_quantize_fit.restype = i32
+    L.mxfp4_quantize_fit.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), i32, vp, vp, vp]
     L.mxfp4_gemm.restype = i32
     L.mxfp4_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, i32, vp, i32, i64, vp]
     L.mxfp4_linear_small.restype = i32
@@ -125,6 +127,24 @@ class Kron:
         return Kron.from_host(a, b, self.a.device)
 
 
+@dataclass
+class Smooth:
+    """Per-channel smoothing: column c is multiplied by r[c] before
+    quantizing (r = 1 / s for smoothing factors s); fp32 device tensor of k
+    factors."""
+    r: torch.Tensor
+
+    @staticmethod
+    def from_host(r: np.ndarray, device="cuda") -> "Smooth":
+        return Smooth(torch.from_numpy(np.ascontiguousarray(r, np.float32).ravel()).to(device))
+
+    def weight_side(self) -> "Smooth":
+        """Factors 1 / r[c] (binary64 reciprocal rounded to fp32), for folding
+        the inverse scaling into W."""
+        r = self.r.cpu().numpy().astype(np.float64)
+        return Smooth.from_host((1.0 / r).astype(np.float32), self.r.device)
+
+
 def _rot_desc(rot, device):
     if rot is None:
         return None, ()
@@ -138,6 +158,11 @@ def _rot_desc(rot, device):
             if t.dtype != torch.float32 or not t.is_contiguous() or t.device != device:
                 raise ValueError("Kron factors must be contiguous fp32 tensors on the input's device")
         return RotationDesc(ROT_KRON, a.shape[0], b.shape[0], 0, a.data_ptr(), b.data_ptr()), (a, b)
+    if isinstance(rot, Smooth):
+        r = rot.r
+        if r.dtype != torch.float32 or not r.is_contiguous() or r.device != device:
+            raise ValueError("smoothing factors must be a contiguous fp32 tensor on the input's device")
+        return RotationDesc(ROT_SMOOTH, 0, 0, 0, r.data_ptr(), None), (r,)
     raise TypeError(f"bad rotation {rot!r}")
 
 
@@ -167,11 +192,12 @@ def _out_shapes(rows: int, k: int, layout: int):
 
 
 def quantize_rotate(x: torch.Tensor, rot=None, codes: torch.Tensor = None, scales: torch.Tensor = None,
-                    layout: int = ROWMAJOR):
+                    layout: int = ROWMAJOR, fit: bool = False):
     """MXFP4-quantize the rows of x (fp32 or bf16, [rows, k], unit column
-    stride) with an optional block rotation.  Returns (codes, scales) uint8:
-    [rows, k/2] and [rows, k/32] (ROWMAJOR), or the same shapes over
-    padded_rows(rows) rows holding the tiled bytes (TILED)."""
+    stride) with an optional block transform (None, "h32", Kron, Smooth).
+    fit=True fits each block exponent (mxfp4_quantize_fit).  Returns (codes,
+    scales) uint8: [rows, k/2] and [rows, k/32] (ROWMAJOR), or the same shapes
+    over padded_rows(rows) rows holding the tiled bytes (TILED)."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, k = x.shape
@@ -185,11 +211,11 @@ def quantize_rotate(x: torch.Tensor, rot=None, codes: torch.Tensor = None, scale
     if tuple(codes.shape) != cshape or tuple(scales.shape) != sshape:
         raise ValueError(f"codes/scales must be {cshape} / {sshape}")
     desc, _keep = _rot_desc(rot, x.device)
-    st = lib().mxfp4_quantize_rotate(
-        x.data_ptr(), _dtype_code(x.dtype), rows, k, x.stride(0),
-        ctypes.byref(desc) if desc is not None else None, layout,
-        codes.data_ptr(), scales.data_ptr(), _stream(x.device))
-    _check(st, "mxfp4_quantize_rotate")
+    fn = lib().mxfp4_quantize_fit if fit else lib().mxfp4_quantize_rotate
+    st = fn(x.data_ptr(), _dtype_code(x.dtype), rows, k, x.stride(0),
+            ctypes.byref(desc) if desc is not None else None, layout,
+            codes.data_ptr(), scales.data_ptr(), _stream(x.device))
+    _check(st, "mxfp4_quantize_fit" if fit else "mxfp4_quantize_rotate")
     return codes, scales
 
 
@@ -263,13 +289,14 @@ def linear_small(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
     return y
 
 
-def quantize_weight(w: torch.Tensor, rot=None, layout: int = ROWMAJOR):
+def quantize_weight(w: torch.Tensor, rot=None, layout: int = ROWMAJOR, fit: bool = False):
     """Offline weight quantization with the weight side of `rot`: the same
-    Hadamard-32 (it is its own inverse-transpose), or the Kronecker factors
-    (A^-T, B^-T), so that each block dot product is preserved."""
-    if isinstance(rot, Kron):
+    Hadamard-32 (it is its own inverse-transpose), the Kronecker factors
+    (A^-T, B^-T), or the reciprocal smoothing factors, so that each block dot
+    product is preserved.  fit=True fits the block exponents."""
+    if isinstance(rot, (Kron, Smooth)):
         rot = rot.weight_side()
-    return quantize_rotate(w, rot, layout=layout)
+    return quantize_rotate(w, rot, layout=layout, fit=fit)
 
 
 def _tiled_index(rows_pad: int, k: int):

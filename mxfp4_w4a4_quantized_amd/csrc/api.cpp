@@ -25,7 +25,8 @@ struct Rot {
 mxfp4_status parse_rotation(const mxfp4_rotation* rot, Rot& r) {
   if (rot == nullptr) return MXFP4_OK;
   r.kind = rot->kind;
-  if (r.kind != MXFP4_ROT_NONE && r.kind != MXFP4_ROT_HADAMARD32 && r.kind != MXFP4_ROT_KRON)
+  if (r.kind != MXFP4_ROT_NONE && r.kind != MXFP4_ROT_HADAMARD32 && r.kind != MXFP4_ROT_KRON &&
+      r.kind != MXFP4_ROT_SMOOTH)
     return MXFP4_ERR_INVALID_ARG;
   if (rot->reserved != 0) return MXFP4_ERR_INVALID_ARG;
   if (r.kind == MXFP4_ROT_KRON) {
@@ -37,7 +38,52 @@ mxfp4_status parse_rotation(const mxfp4_rotation* rot, Rot& r) {
     r.fb = rot->b;
     if (!aligned(r.fa, 4) || !aligned(r.fb, 4)) return MXFP4_ERR_UNSUPPORTED;
   }
+  if (r.kind == MXFP4_ROT_SMOOTH) {
+    if (rot->a == nullptr) return MXFP4_ERR_INVALID_ARG;
+    r.fa = rot->a;
+    if (!aligned(r.fa, 16)) return MXFP4_ERR_UNSUPPORTED;
+  }
   return MXFP4_OK;
+}
+
+}  // namespace
+
+namespace {
+
+mxfp4_status quantize_impl(const void* x, int32_t x_dtype, int64_t rows, int64_t k, int64_t ld_x,
+                           const mxfp4_rotation* rot, int32_t layout, uint8_t* codes, uint8_t* scales,
+                           bool fit, void* stream) {
+  if (x_dtype != MXFP4_F32 && x_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
+  if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
+  const bool tiled = layout == MXFP4_LAYOUT_TILED;
+  if (rows < 0 || k <= 0 || (k % (tiled ? mxfp4::kTileK : 32)) != 0 || ld_x < k) return MXFP4_ERR_INVALID_ARG;
+  Rot r;
+  const mxfp4_status rs = parse_rotation(rot, r);
+  if (rs != MXFP4_OK) return rs;
+  if (rows == 0) return MXFP4_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MXFP4_ERR_INVALID_ARG;
+  const int64_t elem = (x_dtype == MXFP4_BF16) ? 2 : 4;
+  if (!aligned(x, 16) || ((ld_x * elem) % 16) != 0 || !aligned(codes, 16)) return MXFP4_ERR_UNSUPPORTED;
+  if (tiled && !aligned(scales, 4)) return MXFP4_ERR_UNSUPPORTED;
+  const int64_t rows_pad = tiled ? (rows + mxfp4::kTileRows - 1) / mxfp4::kTileRows * mxfp4::kTileRows : rows;
+  if (rows_pad * (k / 32) >= (int64_t(1) << 31)) return MXFP4_ERR_UNSUPPORTED;
+
+  mxfp4::QuantArgs a;
+  a.x = x;
+  a.ld_x = ld_x;
+  a.rows = static_cast<uint32_t>(rows);
+  a.nblk_row = static_cast<uint32_t>(k / 32);
+  a.rot = r.kind;
+  a.p = r.p;
+  a.q = r.q;
+  a.fa = r.fa;
+  a.fb = r.fb;
+  a.codes = codes;
+  a.scales = scales;
+  a.tiled = tiled;
+  a.rows_pad = static_cast<uint32_t>(rows_pad);
+  a.fit = fit;
+  return from_hip(mxfp4::launch_quantize(a, x_dtype == MXFP4_BF16, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -70,36 +116,13 @@ MXFP4_API mxfp4_status mxfp4_tiled_bytes(int64_t rows, int64_t k, int64_t* codes
 MXFP4_API mxfp4_status mxfp4_quantize_rotate(const void* x, int32_t x_dtype, int64_t rows, int64_t k,
                                              int64_t ld_x, const mxfp4_rotation* rot, int32_t layout,
                                              uint8_t* codes, uint8_t* scales, void* stream) {
-  if (x_dtype != MXFP4_F32 && x_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
-  if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
-  const bool tiled = layout == MXFP4_LAYOUT_TILED;
-  if (rows < 0 || k <= 0 || (k % (tiled ? mxfp4::kTileK : 32)) != 0 || ld_x < k) return MXFP4_ERR_INVALID_ARG;
-  Rot r;
-  const mxfp4_status rs = parse_rotation(rot, r);
-  if (rs != MXFP4_OK) return rs;
-  if (rows == 0) return MXFP4_OK;
-  if (x == nullptr || codes == nullptr || scales == nullptr) return MXFP4_ERR_INVALID_ARG;
-  const int64_t elem = (x_dtype == MXFP4_BF16) ? 2 : 4;
-  if (!aligned(x, 16) || ((ld_x * elem) % 16) != 0 || !aligned(codes, 16)) return MXFP4_ERR_UNSUPPORTED;
-  if (tiled && !aligned(scales, 4)) return MXFP4_ERR_UNSUPPORTED;
-  const int64_t rows_pad = tiled ? (rows + mxfp4::kTileRows - 1) / mxfp4::kTileRows * mxfp4::kTileRows : rows;
-  if (rows_pad * (k / 32) >= (int64_t(1) << 31)) return MXFP4_ERR_UNSUPPORTED;
+  return quantize_impl(x, x_dtype, rows, k, ld_x, rot, layout, codes, scales, false, stream);
+}
 
-  mxfp4::QuantArgs a;
-  a.x = x;
-  a.ld_x = ld_x;
-  a.rows = static_cast<uint32_t>(rows);
-  a.nblk_row = static_cast<uint32_t>(k / 32);
-  a.rot = r.kind;
-  a.p = r.p;
-  a.q = r.q;
-  a.fa = r.fa;
-  a.fb = r.fb;
-  a.codes = codes;
-  a.scales = scales;
-  a.tiled = tiled;
-  a.rows_pad = static_cast<uint32_t>(rows_pad);
-  return from_hip(mxfp4::launch_quantize(a, x_dtype == MXFP4_BF16, static_cast<hipStream_t>(stream)));
+MXFP4_API mxfp4_status mxfp4_quantize_fit(const void* x, int32_t x_dtype, int64_t rows, int64_t k,
+                                          int64_t ld_x, const mxfp4_rotation* rot, int32_t layout,
+                                          uint8_t* codes, uint8_t* scales, void* stream) {
+  return quantize_impl(x, x_dtype, rows, k, ld_x, rot, layout, codes, scales, true, stream);
 }
 
 MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,

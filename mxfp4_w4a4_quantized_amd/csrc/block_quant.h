@@ -11,7 +11,14 @@
 //  - power-of-two E8M0 scale: "Bridging the Gap Between Promise and
 //    Performance for Microscaling FP4 Quantization", "Probleemstelling";
 //  - Hadamard-32 micro-rotation: same page, "Methodologie: MR-GPTQ" item 1;
-//  - Kronecker block transform: "KroQuant: ...", abstract and "Tiefenanalyse".
+//  - Kronecker block transform: "KroQuant: ...", abstract and "Tiefenanalyse";
+//  - per-channel smoothing, the SmoothQuant baseline that page compares with:
+//    one fp32 multiply by the caller's per-channel factor;
+//  - scale fitting: "Bridging the Gap ...", "Methodologie: MR-GPTQ" item 2
+//    (the exponent of the block scale re-fitted to the data; the rule used
+//    here: the exponent among e0 - 1, e0, e0 + 1 with the smallest squared
+//    error, each error summed in binary64 in element order, ties keep e0,
+//    then e0 + 1).
 //
 // Every fp32 operation is a single IEEE operation in a fixed order (the
 // library is compiled with -ffp-contract=off and the only fused operations
@@ -78,24 +85,29 @@ __device__ __forceinline__ void kron32(const float* __restrict__ fa, const float
   }
 }
 
-// Block amax, E8M0 scale byte and packed E2M1 codes of one rotated block:
-// returns the scale byte, writes the 16 code bytes (element 2j in the low
-// nibble of byte j) to w.
-__device__ __forceinline__ uint32_t encode_block(const float (&v)[32], uint32_t (&w)[4]) {
-  // block amax (exact)
-  float amax = 0.0f;
+// E8M0 byte of the block rule: floor(log2 amax) - 2 clamped at -127 is the
+// biased exponent field of amax minus 2 (subnormal and zero amax have field 0
+// and clamp).
+__device__ __forceinline__ uint32_t rule_sbyte(const float (&v)[32]) {
+  float amax = 0.0f;   // exact
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-
-  // E8M0: floor(log2 amax) - 2 clamped at -127 is the biased exponent field
-  // of amax minus 2 (subnormal and zero amax have field 0 and clamp).
   const uint32_t ef = __float_as_uint(amax) >> 23;
-  const uint32_t sbyte = ef > 2u ? ef - 2u : 0u;
-  // The block scale 2^e as fp32 (2^-127 is the subnormal 0x00400000).  The
-  // converter divides by its scale operand exactly -- it equals converting
-  // v * 2^-e with scale 1 for every finite input, checked on the device for
-  // all bf16 values and e in [-127, 125] -- so no separate multiply is needed.
-  const float scale = __uint_as_float(sbyte ? sbyte << 23 : 0x00400000u);
+  return ef > 2u ? ef - 2u : 0u;
+}
+
+// The block scale 2^(sbyte - 127) as fp32 (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float scale_of(uint32_t sbyte) {
+  return __uint_as_float(sbyte ? sbyte << 23 : 0x00400000u);
+}
+
+// Packed E2M1 codes (element 2j in the low nibble of byte j) of the block at
+// scale byte sbyte.  The converter divides by its scale operand exactly -- it
+// equals converting v * 2^-e with scale 1 for every finite input, checked on
+// the device for all bf16 values and e in [-127, 125] -- then rounds to
+// nearest even and saturates, keeping the sign of values that round to zero.
+__device__ __forceinline__ void encode_at(const float (&v)[32], uint32_t sbyte, uint32_t (&w)[4]) {
+  const float scale = scale_of(sbyte);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t acc = 0;
@@ -105,15 +117,82 @@ __device__ __forceinline__ uint32_t encode_block(const float (&v)[32], uint32_t 
     acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, v[8 * i + 6], v[8 * i + 7], scale, 3);
     w[i] = acc;
   }
+}
+
+// Block amax, E8M0 scale byte and packed E2M1 codes of one rotated block:
+// returns the scale byte, writes the 16 code bytes to w.
+__device__ __forceinline__ uint32_t encode_block(const float (&v)[32], uint32_t (&w)[4]) {
+  const uint32_t sbyte = rule_sbyte(v);
+  encode_at(v, sbyte, w);
   return sbyte;
 }
 
-// Rotation of one block: 0 none, 1 Hadamard-32, 2 Kronecker P x Q.
+// Value of a 4-bit E2M1 code (bit 3 the sign).
+__device__ __forceinline__ double e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const double mag = m < 4u ? 0.5 * (double)m : (m == 4u ? 2.0 : (m == 5u ? 3.0 : (m == 6u ? 4.0 : 6.0)));
+  return (c & 8u) ? -mag : mag;
+}
+
+// Squared error of the block encoded at scale byte sbyte, in binary64: over
+// the elements in order, d = v - x_hat (x_hat = code value * scale, exact),
+// s = s + d * d, each a single binary64 operation.
+__device__ __forceinline__ double block_sse(const float (&v)[32], uint32_t sbyte) {
+  uint32_t w[4];
+  encode_at(v, sbyte, w);
+  const double sc = (double)scale_of(sbyte);
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = (w[i >> 3] >> (4 * (i & 7))) & 0xFu;
+    const double xh = e2m1_value(c) * sc;
+    const double d = (double)v[i] - xh;
+    const double d2 = d * d;
+    s = s + d2;
+  }
+  return s;
+}
+
+// Scale-fitted encoding of one block (see the header comment for the rule).
+__device__ __forceinline__ uint32_t encode_block_fit(const float (&v)[32], uint32_t (&w)[4]) {
+  const uint32_t s0 = rule_sbyte(v);
+  uint32_t best = s0;
+  double err = block_sse(v, s0);
+  const double e_up = block_sse(v, s0 + 1u);
+  if (e_up < err) {
+    err = e_up;
+    best = s0 + 1u;
+  }
+  if (s0 > 0u) {
+    const double e_dn = block_sse(v, s0 - 1u);
+    if (e_dn < err) best = s0 - 1u;
+  }
+  encode_at(v, best, w);
+  return best;
+}
+
+template <bool FIT>
+__device__ __forceinline__ uint32_t encode_block_sel(const float (&v)[32], uint32_t (&w)[4]) {
+  if constexpr (FIT) return encode_block_fit(v, w);
+  else return encode_block(v, w);
+}
+
+// Transform of one block: 0 none, 1 Hadamard-32, 2 Kronecker P x Q (factors
+// fa, fb), 3 per-channel smoothing (fa = this block's 32 factors).
 template <int ROT, int P, int Q>
 __device__ __forceinline__ void rotate_block(const float* __restrict__ fa, const float* __restrict__ fb,
                                              float (&v)[32]) {
   if constexpr (ROT == 1) hadamard32(v);
   if constexpr (ROT == 2) kron32<P, Q>(fa, fb, v);
+  if constexpr (ROT == 3) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f4 r = *reinterpret_cast<const f4*>(fa + 4 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * i + j] = v[4 * i + j] * r[j];
+    }
+  }
 }
 
 }  // namespace blockq

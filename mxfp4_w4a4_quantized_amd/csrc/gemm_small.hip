@@ -296,10 +296,10 @@ void launch_mg(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s)
 // quantize while the weights stream in from HBM.  NG weight groups of 16 rows
 // per workgroup (32 rows for M <= 32) keep the redundant per-workgroup
 // quantization to N / (16 NG) copies; KC = 4 steps per wave keeps the
-// registers within two waves per SIMD.  Activations are bf16; the rotation is
-// none, Hadamard-32 or a Kronecker product with 2 <= P <= 16 (the factors sit
-// in scalar registers; the degenerate 1 x 32 and 32 x 1 forms, a dense 32 x 32
-// factor, are left to the separate quantizer).
+// registers within two waves per SIMD.  Activations are bf16; the transform
+// is none, Hadamard-32, per-channel smoothing or a Kronecker product with
+// 2 <= P <= 16 (the factors sit in scalar registers; the degenerate 1 x 32 and
+// 32 x 1 forms, a dense 32 x 32 factor, are left to the separate quantizer).
 constexpr int KC = 4;          // K steps per fused chunk
 
 template <bool XBF16>
@@ -405,7 +405,11 @@ __global__ __launch_bounds__(64 * MAXW) void linear_small_kernel(LinearArgs L, i
       u32x4 xf[KC];
       int xs[KC];
 #pragma unroll
-      for (int j = 0; j < KC; ++j) quantize_raw<XBF16, ROT, P, Q>(raw[j], L.fa, L.fb, xf[j], xs[j]);
+      for (int j = 0; j < KC; ++j) {
+        // smoothing: this lane's block column picks its 32 factors
+        const int col = min(4 * (s0 + j) + lg, kblocks - 1);
+        quantize_raw<XBF16, ROT, P, Q>(raw[j], ROT == 3 ? L.fa + 32 * col : L.fa, L.fb, xf[j], xs[j]);
+      }
 #pragma unroll
       for (int j = 0; j < KC; ++j)
         if (s0 + j < s_end) {
@@ -452,6 +456,7 @@ template <int MG, int NG, bool XBF16>
 hipError_t launch_fused_rot(const LinearArgs& L, int nwaves, int spw, int y_vec, hipStream_t s) {
   if (L.rot == 0) launch_fused<MG, NG, XBF16, 0, 1, 32>(L, nwaves, spw, y_vec, s);
   else if (L.rot == 1) launch_fused<MG, NG, XBF16, 1, 1, 32>(L, nwaves, spw, y_vec, s);
+  else if (L.rot == 3) launch_fused<MG, NG, XBF16, 3, 1, 32>(L, nwaves, spw, y_vec, s);
   else {
     switch (L.p) {
       case 2: launch_fused<MG, NG, XBF16, 2, 2, 16>(L, nwaves, spw, y_vec, s); break;

@@ -13,8 +13,9 @@ struct QuantArgs {
   uint32_t nblk_row;   // k / 32
   int32_t rot;         // mxfp4_rot_kind
   int32_t p, q;        // Kronecker factor sizes
-  const float* fa;     // p x p
+  const float* fa;     // p x p (Kronecker), or k per-channel factors (smoothing)
   const float* fb;     // q x q
+  bool fit;            // fitted block exponents instead of the E8M0 rule
   uint8_t* codes;
   uint8_t* scales;
   bool tiled;          // MXFP4_LAYOUT_TILED outputs (nblk_row % 4 == 0)

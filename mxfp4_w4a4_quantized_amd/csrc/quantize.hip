@@ -55,7 +55,8 @@ __device__ __forceinline__ int slab_swz(int blk) {
 // row r's 64 bytes.
 __device__ __forceinline__ int tiled_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
-// rot: 0 none, 1 Hadamard-32, 2 Kronecker (P x Q)
+// rot: 0 none, 1 Hadamard-32, 2 Kronecker (P x Q), 3 per-channel smoothing;
+// FIT: fitted block exponents (offline weight quantization).
 //
 // Work split: every wave quantizes 64 blocks.  Row-major output: 64
 // consecutive blocks in row-major block order.  Tiled output: the 4 blocks of
@@ -63,7 +64,7 @@ __device__ __forceinline__ int tiled_swz(int r) { return ((r >> 1) ^ (r >> 2)) &
 // one contiguous KiB of the tiled layout.  Padding rows inside the last
 // 16-row group load as zeros and store zero codes and scales; the 16-row
 // groups past it are not written at all (no GEMM output depends on them).
-template <bool BF16, int ROT, int P, int Q>
+template <bool BF16, int ROT, int P, int Q, bool FIT>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int dense) {
   constexpr int CPB = BF16 ? 4 : 8;   // 16-byte chunks per 32-element block
   __shared__ u32x4 slab[kThreads / 64][64 * CPB];
@@ -145,9 +146,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
       for (int j = 0; j < 4; ++j) v[4 * i + j] = __uint_as_float(q4[i][j]);
   }
 
-  rotate_block<ROT, P, Q>(a.fa, a.fb, v);
+  // smoothing factors of this block's 32 channels (block column within its row)
+  const uint32_t kcol = (!a.tiled && dense) ? ocol % a.nblk_row : ocol;
+  rotate_block<ROT, P, Q>(ROT == 3 ? a.fa + 32 * kcol : a.fa, a.fb, v);
   uint32_t w[4];
-  const uint32_t sbyte = encode_block(v, w);
+  const uint32_t sbyte = encode_block_sel<FIT>(v, w);
   if (a.tiled) {
     const uint32_t t = orow / kTileRows, r = orow % kTileRows, sg = ocol / 4, cb = ocol % 4;
     const uint64_t ts = (uint64_t)t * nstage + sg;   // (tile, stage) index
@@ -162,24 +165,26 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool FIT>
 hipError_t dispatch(const QuantArgs& a, hipStream_t s) {
   const uint64_t rows = a.tiled ? (a.rows + 15) / 16 * 16 : a.rows;   // tiled: whole 16-row groups
   const uint64_t blocks = rows * a.nblk_row;   // 64 per wave
   const dim3 grid((uint32_t)((blocks + kThreads - 1) / kThreads)), block(kThreads);
   const int dense = a.ld_x == (int64_t)a.nblk_row * 32;
   if (a.rot == 0) {
-    quantize_kernel<BF16, 0, 1, 32><<<grid, block, 0, s>>>(a, dense);
+    quantize_kernel<BF16, 0, 1, 32, FIT><<<grid, block, 0, s>>>(a, dense);
   } else if (a.rot == 1) {
-    quantize_kernel<BF16, 1, 1, 32><<<grid, block, 0, s>>>(a, dense);
+    quantize_kernel<BF16, 1, 1, 32, FIT><<<grid, block, 0, s>>>(a, dense);
+  } else if (a.rot == 3) {
+    quantize_kernel<BF16, 3, 1, 32, FIT><<<grid, block, 0, s>>>(a, dense);
   } else {
     switch (a.p) {
-      case 1: quantize_kernel<BF16, 2, 1, 32><<<grid, block, 0, s>>>(a, dense); break;
-      case 2: quantize_kernel<BF16, 2, 2, 16><<<grid, block, 0, s>>>(a, dense); break;
-      case 4: quantize_kernel<BF16, 2, 4, 8><<<grid, block, 0, s>>>(a, dense); break;
-      case 8: quantize_kernel<BF16, 2, 8, 4><<<grid, block, 0, s>>>(a, dense); break;
-      case 16: quantize_kernel<BF16, 2, 16, 2><<<grid, block, 0, s>>>(a, dense); break;
-      case 32: quantize_kernel<BF16, 2, 32, 1><<<grid, block, 0, s>>>(a, dense); break;
+      case 1: quantize_kernel<BF16, 2, 1, 32, FIT><<<grid, block, 0, s>>>(a, dense); break;
+      case 2: quantize_kernel<BF16, 2, 2, 16, FIT><<<grid, block, 0, s>>>(a, dense); break;
+      case 4: quantize_kernel<BF16, 2, 4, 8, FIT><<<grid, block, 0, s>>>(a, dense); break;
+      case 8: quantize_kernel<BF16, 2, 8, 4, FIT><<<grid, block, 0, s>>>(a, dense); break;
+      case 16: quantize_kernel<BF16, 2, 16, 2, FIT><<<grid, block, 0, s>>>(a, dense); break;
+      case 32: quantize_kernel<BF16, 2, 32, 1, FIT><<<grid, block, 0, s>>>(a, dense); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -190,7 +195,8 @@ hipError_t dispatch(const QuantArgs& a, hipStream_t s) {
 
 hipError_t launch_quantize(const QuantArgs& a, bool bf16, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
-  return bf16 ? dispatch<true>(a, s) : dispatch<false>(a, s);
+  if (a.fit) return bf16 ? dispatch<true, true>(a, s) : dispatch<false, true>(a, s);
+  return bf16 ? dispatch<true, false>(a, s) : dispatch<false, false>(a, s);
 }
 
 }  // namespace mxfp4

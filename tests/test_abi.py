@@ -84,6 +84,21 @@ def test_quantize_argument_errors():
     assert q(A, 1, 4, 64, 64, ctypes.byref(kr), R, A, A, None) == INV     # reserved != 0
 
 
+def test_smooth_and_fit_argument_errors():
+    INV, UNS = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED
+    A, R = ALIGNED, mx.ROWMAJOR
+    sm = mx.RotationDesc(mx.ROT_SMOOTH, 0, 0, 0, None, None)
+    assert q(A, 1, 4, 64, 64, ctypes.byref(sm), R, A, A, None) == INV        # null factors
+    sm = mx.RotationDesc(mx.ROT_SMOOTH, 0, 0, 0, A + 4, None)
+    assert q(A, 1, 4, 64, 64, ctypes.byref(sm), R, A, A, None) == UNS        # factors not 16 B aligned
+    fit = mx.lib().mxfp4_quantize_fit
+    assert fit(A, 7, 4, 64, 64, None, R, A, A, None) == INV                  # same checks as quantize
+    assert fit(A, 1, 4, 48, 64, None, R, A, A, None) == INV
+    assert fit(NULL, 1, 4, 64, 64, None, R, A, A, None) == INV
+    assert fit(MISALIGNED, 1, 4, 64, 64, None, R, A, A, None) == UNS
+    assert fit(NULL, 1, 0, 64, 64, None, R, NULL, NULL, None) == mx.MXFP4_OK
+
+
 def test_gemm_argument_errors():
     INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
     A, R, T = ALIGNED, mx.ROWMAJOR, mx.TILED

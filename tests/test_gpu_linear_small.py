@@ -39,9 +39,12 @@ def bf16_dev(x_bits):
     return to_dev(x_bits.view(np.int16)).view(torch.bfloat16)
 
 
-def make_rot(r, seed=5):
+def make_rot(r, seed=5, k=None):
     if r is None or r == "h32":
         return r
+    if r == "smooth":
+        rng = np.random.default_rng(seed)
+        return mx.Smooth.from_host((0.25 + 4 * rng.random(k)).astype(np.float32), DEV)
     p, q = r
     rng = np.random.default_rng(seed)
     a = (np.eye(p) + 0.1 * rng.standard_normal((p, p))).astype(np.float32)
@@ -52,6 +55,8 @@ def make_rot(r, seed=5):
 def oracle_rot(rot):
     if rot is None or rot == "h32":
         return rot
+    if isinstance(rot, mx.Smooth):
+        return ("smooth", rot.r.cpu().numpy())
     return ("kron", rot.a.cpu().numpy(), rot.b.cpu().numpy())
 
 
@@ -73,7 +78,7 @@ def norm_err(got, ref, na, nb):
     return float(rel.max()) if rel.size else 0.0
 
 
-ROTS = [None, "h32", (2, 16), (4, 8), (8, 4), (16, 2)]
+ROTS = [None, "h32", "smooth", (2, 16), (4, 8), (8, 4), (16, 2)]
 
 
 @pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
@@ -83,7 +88,7 @@ def test_fused_quantization_is_bit_exact(rot, m, layout):
     k = 512
     rng = np.random.default_rng(m * 7 + k)
     x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
-    r = make_rot(rot)
+    r = make_rot(rot, k=k)
     xc, xs = oracle.quantize(x, rot=oracle_rot(r), bf16=True)
     want = oracle.dequantize(xc, xs)                       # exact in binary64 and in fp32
     wc, ws = oracle.quantize(np.eye(k, dtype=np.float32))  # identity weights, no rotation
@@ -104,13 +109,13 @@ SHAPES = [
     (16, 14336, 4096, "tiled"), (33, 70, 2048, "tiled")]
 
 
-@pytest.mark.parametrize("rot", [None, "h32", (4, 8)], ids=str)
+@pytest.mark.parametrize("rot", [None, "h32", "smooth", (4, 8)], ids=str)
 @pytest.mark.parametrize("m,n,k,layout", SHAPES)
 def test_fused_linear_matches_oracle(m, n, k, layout, rot):
     rng = np.random.default_rng(m + 3 * n + k)
     x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
     wc, ws = workloads.random_mxfp4(rng, n, k)
-    r = make_rot(rot)
+    r = make_rot(rot, k=k)
     lay = LAYOUTS[layout]
     announce("linear_small", m, n, k, layout, rot)
     dwc, dws = weights_dev(wc, ws, lay)

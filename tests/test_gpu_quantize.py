@@ -194,5 +194,110 @@ def test_errors_raise():
     with pytest.raises(mx.Mxfp4Error):
         mx.quantize_rotate(x)
 
+# ------------------------------------------------- smoothing and scale fitting ---
+
+def rand_smooth(k, seed):
+    rng = np.random.default_rng(seed)
+    return mx.Smooth.from_host((0.25 + 4 * rng.random(k)).astype(np.float32), DEV)
+
+
+def oracle_rot_any(rot):
+    if isinstance(rot, mx.Smooth):
+        return ("smooth", rot.r.cpu().numpy())
+    return oracle_rot(rot)
+
+
+def make_rot(kind, k, seed):
+    if kind == "kron":
+        return rand_kron(4, 8, seed)
+    if kind == "smooth":
+        return rand_smooth(k, seed)
+    return kind
+
+
+def quantize_both(x_host, bf16, rot, layout, fit):
+    rows, k = x_host.shape
+    announce("quantize", "fit" if fit else "", rot if isinstance(rot, (str, type(None))) else type(rot).__name__,
+             rows, k, "bf16" if bf16 else "f32", "tiled" if layout == mx.TILED else "rowmajor")
+    c, s = mx.quantize_rotate(dev_x(x_host, bf16), rot, layout=layout, fit=fit)
+    torch.cuda.synchronize()
+    got = (c.cpu().numpy(), s.cpu().numpy())
+    if layout == mx.TILED:
+        got = mx.untile_host(got[0], got[1], rows)
+    ref = oracle.quantize(x_host, rot=oracle_rot_any(rot), bf16=bf16, fit=fit)
+    return got, ref
+
+
+@pytest.mark.parametrize("layout", [mx.ROWMAJOR, mx.TILED])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("rows,k", [(3, 128), (70, 512), (300, 3072)])
+def test_smooth_matches_oracle(rows, k, bf16, layout):
+    rng = np.random.default_rng(rows + k + bf16)
+    x = workloads.random_blocks(rng, rows, k)
+    if bf16:
+        x = workloads.bf16_bits(x)
+    got, ref = quantize_both(x, bf16, rand_smooth(k, rows * 3 + k), layout, False)
+    assert_same(got, ref, f"smooth {rows}x{k}")
+
+
+def test_smooth_strided_rows():
+    # ld_x > k: the kernel's non-dense block addressing picks each block's factors
+    rng = np.random.default_rng(12)
+    full = workloads.bf16_bits(workloads.random_blocks(rng, 33, 640))
+    r = rand_smooth(256, 13)
+    x = dev_x(full, True)[:, :256]
+    announce("quantize smooth strided", x.shape, x.stride())
+    c, s = mx.quantize_rotate(x, r)
+    ref = oracle.quantize(np.ascontiguousarray(full[:, :256]), rot=oracle_rot_any(r), bf16=True)
+    assert_same((c.cpu().numpy(), s.cpu().numpy()), ref, "smooth strided")
+
+
+@pytest.mark.parametrize("layout", [mx.ROWMAJOR, mx.TILED])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("rot", [None, "h32", "kron", "smooth"])
+def test_fit_matches_oracle(rot, bf16, layout):
+    rng = np.random.default_rng(20 + bf16)
+    rows, k = 257, 1024
+    x = workloads.random_blocks(rng, rows, k)
+    x[rng.random(x.shape) < 0.05] *= np.float32(9.0)      # outliers inside blocks
+    if bf16:
+        x = workloads.bf16_bits(x)
+    got, ref = quantize_both(x, bf16, make_rot(rot, k, 31), layout, True)
+    assert_same(got, ref, f"fit {rot}")
+    # the fitted exponents differ from the plain rule somewhere (the test bites)
+    plain = oracle.quantize(x, rot=oracle_rot_any(make_rot(rot, k, 31)), bf16=bf16)
+    assert np.count_nonzero(plain[1] != ref[1]) > 0
+
+
+def test_fit_edge_blocks():
+    for bf16 in (False, True):
+        x = edge_blocks()
+        if bf16:
+            x = workloads.bf16_bits(x)
+        got, ref = quantize_both(x, bf16, None, mx.ROWMAJOR, True)
+        assert_same(got, ref, "fit edge")
+
+
+def test_smoothed_linear_matches_oracle():
+    """A smoothed linear layer: activations multiplied by r per channel, the
+    weights by 1/r (binary64 reciprocal rounded to fp32); the GEMM of the two
+    quantized operands against the oracle's."""
+    rng = np.random.default_rng(40)
+    m, n, k = 300, 260, 512
+    x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    sm = rand_smooth(k, 41)
+    announce("smoothed linear", m, n, k)
+    wc, ws = mx.quantize_weight(torch.from_numpy(w).to(DEV), sm)
+    y = mx.linear(dev_x(x, True), wc, ws, sm, torch.float32)
+    torch.cuda.synchronize()
+    xc, xs = oracle.quantize(x, rot=oracle_rot_any(sm), bf16=True)
+    rwc, rws = oracle.quantize(w, rot=oracle_rot_any(sm.weight_side()))
+    assert np.array_equal(wc.cpu().numpy(), rwc) and np.array_equal(ws.cpu().numpy(), rws)
+    ref = oracle.gemm(xc, xs, rwc, rws)
+    den = np.outer(np.sqrt((oracle.dequantize(xc, xs) ** 2).sum(1)), np.sqrt((oracle.dequantize(rwc, rws) ** 2).sum(1)))
+    assert (np.abs(y.cpu().numpy() - ref) <= 1e-5 * den).all()
+
+
 # Full-size workloads (both operands, every code and scale byte) are checked
 # in test_gpu_gemm.test_full_workload_linear, in the benchmark's launch setup.
