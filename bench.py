@@ -32,6 +32,9 @@ Prints one JSON line:
   weight_fit  offline weight quantization with the E8M0 rule and with fitted
               block exponents: time, and the squared error of each against the
               weight-side transformed fp32 weights
+  mxfp4_out   the same GEMM writing MXFP4 (mxfp4_gemm_requant, Y requantized
+              per 32-block in the epilogue) beside the bf16-output GEMM, both
+              timed back to back over the buffer sets
   copy_gbps   a plain device copy in the same run (practical HBM ceiling)
   cpu_baseline  the CPU oracle on the same workload (all rows by default)
 
@@ -233,6 +236,19 @@ def gpu_leg(name: str, steps: int, warmup: int):
         tms = time_parts(lambda s_, r_=trot: mx.quantize_rotate(s_["x"], r_, s_["xc"], s_["xs"], layout=lay))
         transforms[tname] = tms
 
+    # --- the same GEMM with an MXFP4 output (requantized in the epilogue)
+    requant_ms = None
+    if not use_fused and n % 256 == 0 and k % 128 == 0:
+        qc_out = torch.empty((mx.padded_rows(m), n // 2), dtype=torch.uint8, device=dev)
+        qs_out = torch.empty((mx.padded_rows(m), n // 32), dtype=torch.uint8, device=dev)
+        requant_ms = time_parts(lambda s_: mx.gemm_requant(s_["xc"], s_["xs"], s_["wc"], s_["ws"], layout=lay,
+                                                             out_layout=lay, m=m, n=n, y_codes=qc_out,
+                                                             y_scales=qs_out))
+        gemm_ms = time_parts(lambda s_: mx.gemm(s_["xc"], s_["xs"], s_["wc"], s_["ws"], out_dtype, s_["y"],
+                                                 layout=lay))
+        requant_ms = (requant_ms, gemm_ms)
+        del qc_out, qs_out
+
     # --- offline weight quantization: plain E8M0 rule vs fitted exponents, and
     # the squared error of each against the (transformed) fp32 weights
     w32 = torch.from_numpy(inp["w"]).to(dev)
@@ -275,7 +291,7 @@ def gpu_leg(name: str, steps: int, warmup: int):
 
     props = torch.cuda.get_device_properties(dev)
     return dict(m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms,
-                fused=fused_res, copy_gbps=copy_gbps, transforms=transforms, wfit=wfit, nsets=nsets, device=props.name,
+                fused=fused_res, copy_gbps=copy_gbps, transforms=transforms, wfit=wfit, requant=requant_ms, nsets=nsets, device=props.name,
                 cus=props.multi_processor_count, arch=getattr(props, "gcnArchName", ""))
 
 
@@ -418,6 +434,10 @@ def main():
         "weight_fit": {"plain_ms": round(g["wfit"]["plain"]["ms"], 3), "fit_ms": round(g["wfit"]["fit"]["ms"], 3),
                        "sse_plain": g["wfit"]["plain"]["sse"], "sse_fit": g["wfit"]["fit"]["sse"],
                        "sse_ratio": round(g["wfit"]["fit"]["sse"] / max(g["wfit"]["plain"]["sse"], 1e-300), 4)},
+        "mxfp4_out": None if g["requant"] is None else {
+            "us_per_launch": round(g["requant"][0] * 1e3, 2),
+            "same_gemm_bf16_out_us": round(g["requant"][1] * 1e3, 2),
+            "y_bytes": m * (n // 2 + n // 32), "y_bytes_bf16": m * n * 2},
         "copy_gbps": round(g["copy_gbps"], 1),
         "device": {"name": g["device"], "arch": g["arch"], "cus": g["cus"]},
     }

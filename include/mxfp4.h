@@ -194,6 +194,28 @@ MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
                                   int64_t k, int32_t layout, void* y, int32_t y_dtype, int64_t ld_y,
                                   void* stream);
 
+/* Y = A * B^T with an MXFP4 output: the GEMM's fp32 result is requantized in
+ * the epilogue, per 32-element block along N (the next layer's K), by the
+ * quantizer's rule (E8M0 from the block amax, RNE-saturating E2M1 codes; no
+ * rotation), so the next layer reads MXFP4 activations without a bf16 round
+ * trip.  The codes and scales equal mxfp4_quantize_rotate applied to the fp32
+ * Y of mxfp4_gemm bit for bit.  The pages' kernel "produces output without
+ * conversion back to FP16 or BF16" ("AMD Quark delivers MXFP4 quantization for
+ * FLUX.1-dev ...", "MXFP4 quantization for diffusion models"); this entry point
+ * is that reading of it.
+ *   a_*, b_*, m, n, k, layout  as for mxfp4_gemm; k a multiple of 128.
+ *   y_codes/y_scales  device (written): Y in `y_layout` -- ROWMAJOR
+ *           [m][n/2] and [m][n/32], or TILED with m rows (padding rows not
+ *           written).  16-byte aligned codes, 4-byte aligned scales.
+ * Errors: INVALID_ARG for null pointers (when m, n > 0), bad layouts, k <= 0
+ *   or k % 32 (k % 128 for TILED operands), negative sizes; UNSUPPORTED for
+ *   n % 32 != 0 (n % 128 for a TILED output), k % 128 != 0, misaligned
+ *   pointers or sizes >= 2^30; HIP if the launch fails. */
+MXFP4_API mxfp4_status mxfp4_gemm_requant(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
+                                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
+                                          int64_t k, int32_t layout, uint8_t* y_codes, uint8_t* y_scales,
+                                          int32_t y_layout, void* stream);
+
 /* Fused small-M linear layer Y = Q(rot(X)) * W^T for decode shapes: the
  * activations are rotated and quantized inside the GEMM, each block straight
  * into the matrix-core operand registers, so the quantized activations never

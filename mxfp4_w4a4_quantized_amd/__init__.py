@@ -45,7 +45,8 @@ TILE_ROWS, TILE_K = 256, 128
 
 HADAMARD32 = "h32"
 
-EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_quantize_fit", "mxfp4_gemm", "mxfp4_linear_small", "mxfp4_tiled_bytes",
+EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_quantize_fit", "mxfp4_gemm", "mxfp4_gemm_requant",
+            "mxfp4_linear_small", "mxfp4_tiled_bytes",
             "mxfp4_inverse_transpose", "mxfp4_status_string", "mxfp4_abi_version")
 LINEAR_SMALL_MAX_M = 64
 
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.mxfp4_quantize_fit.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), i32, vp, vp, vp]
     L.mxfp4_gemm.restype = i32
     L.mxfp4_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, i32, vp, i32, i64, vp]
+    L.mxfp4_gemm_requant.restype = i32
+    L.mxfp4_gemm_requant.argtypes = [vp, vp, i64, vp, vp, i64, i64, i32, vp, vp, i32, vp]
     L.mxfp4_linear_small.restype = i32
     L.mxfp4_linear_small.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), vp, vp, i64, i32,
                                      vp, i32, i64, vp]
@@ -247,6 +250,35 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b
                           y.data_ptr(), _dtype_code(y.dtype), y.stride(0), _stream(a_codes.device))
     _check(st, "mxfp4_gemm")
     return y
+
+
+def gemm_requant(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
+                 layout: int = ROWMAJOR, out_layout: int = ROWMAJOR, m: int = None, n: int = None,
+                 y_codes: torch.Tensor = None, y_scales: torch.Tensor = None):
+    """Y = A * B^T requantized to MXFP4 in the GEMM epilogue (n % 32 == 0, or
+    n % 128 == 0 for a TILED output; k % 128 == 0).  Returns (codes, scales) of Y in `out_layout`, the same
+    bytes as quantize_rotate(fp32 Y)."""
+    k = a_codes.shape[1] * 2
+    if m is None:
+        m = a_codes.shape[0]
+    if n is None:
+        n = b_codes.shape[0]
+    for rows, c, sc, name in ((m, a_codes, a_scales, "A"), (n, b_codes, b_scales, "B")):
+        cshape, sshape = _out_shapes(rows, k, layout)
+        if tuple(c.shape) != cshape or tuple(sc.shape) != sshape:
+            raise ValueError(f"operand {name}: codes/scales must be {cshape} / {sshape}")
+    cshape, sshape = _out_shapes(m, n, out_layout)
+    if y_codes is None:
+        y_codes = torch.empty(cshape, dtype=torch.uint8, device=a_codes.device)
+    if y_scales is None:
+        y_scales = torch.empty(sshape, dtype=torch.uint8, device=a_codes.device)
+    if tuple(y_codes.shape) != cshape or tuple(y_scales.shape) != sshape:
+        raise ValueError(f"output codes/scales must be {cshape} / {sshape}")
+    st = lib().mxfp4_gemm_requant(a_codes.data_ptr(), a_scales.data_ptr(), m, b_codes.data_ptr(),
+                                  b_scales.data_ptr(), n, k, layout, y_codes.data_ptr(), y_scales.data_ptr(),
+                                  out_layout, _stream(a_codes.device))
+    _check(st, "mxfp4_gemm_requant")
+    return y_codes, y_scales
 
 
 def linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, rot=None,

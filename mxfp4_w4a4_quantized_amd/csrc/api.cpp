@@ -158,6 +158,44 @@ MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
   return from_hip(mxfp4::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
+MXFP4_API mxfp4_status mxfp4_gemm_requant(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
+                                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, int64_t k,
+                                          int32_t layout, uint8_t* y_codes, uint8_t* y_scales, int32_t y_layout,
+                                          void* stream) {
+  if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
+  if (y_layout != MXFP4_LAYOUT_ROWMAJOR && y_layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
+  const bool tiled = layout == MXFP4_LAYOUT_TILED;
+  if (m < 0 || n < 0 || k <= 0 || (k % (tiled ? mxfp4::kTileK : 32)) != 0) return MXFP4_ERR_INVALID_ARG;
+  if (m == 0 || n == 0) return MXFP4_OK;
+  if (a_codes == nullptr || a_scales == nullptr || b_codes == nullptr || b_scales == nullptr ||
+      y_codes == nullptr || y_scales == nullptr)
+    return MXFP4_ERR_INVALID_ARG;
+  if (m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return MXFP4_ERR_UNSUPPORTED;
+  if ((n % (y_layout == MXFP4_LAYOUT_TILED ? mxfp4::kTileK : 32)) != 0 || (k % mxfp4::kTileK) != 0)
+    return MXFP4_ERR_UNSUPPORTED;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(y_codes, 16)) return MXFP4_ERR_UNSUPPORTED;
+  if (!aligned(a_scales, 4) || !aligned(b_scales, 4) || !aligned(y_scales, 4)) return MXFP4_ERR_UNSUPPORTED;
+
+  mxfp4::GemmArgs g;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.b_codes = b_codes;
+  g.b_scales = b_scales;
+  g.m = static_cast<int32_t>(m);
+  g.n = static_cast<int32_t>(n);
+  g.k = static_cast<int32_t>(k);
+  g.y = nullptr;
+  g.ld_y = n;
+  g.y_bf16 = false;
+  g.tiled = tiled;
+  g.q_out = true;
+  g.q_tiled = (y_layout == MXFP4_LAYOUT_TILED);
+  g.q_codes = y_codes;
+  g.q_scales = y_scales;
+  if (!mxfp4::gemm_large_supported(g)) return MXFP4_ERR_UNSUPPORTED;
+  return from_hip(mxfp4::launch_gemm_large(g, static_cast<hipStream_t>(stream)));
+}
+
 MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t ld_x,
                                           const mxfp4_rotation* rot, const uint8_t* w_codes,
                                           const uint8_t* w_scales, int64_t n, int32_t layout, void* y,

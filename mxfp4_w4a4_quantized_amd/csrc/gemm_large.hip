@@ -62,6 +62,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 256;                      // weight rows per tile
 constexpr int BM = 256;                      // activation rows per tile
@@ -146,7 +147,8 @@ __device__ __forceinline__ void sched_substep() {
 constexpr int WN = MXFP4_GEMM_WN, WM = MXFP4_GEMM_WM;
 constexpr int NT = 64 * WN * WM;
 
-template <bool BF16OUT>
+// OUT: 0 fp32 Y, 1 bf16 Y, 2 MXFP4 Y (requantized per 32-block along N).
+template <int OUT>
 __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles_m, int tiles_n, int grid,
                                                            int xcd_remap, int y_vec) {
   constexpr int NW = WN * WM;
@@ -168,7 +170,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
   const int total = ((ntiles - slot + grid - 1) / grid) * nk;
   const uint32_t kbytes = (uint32_t)g.k / 2, kblocks = (uint32_t)g.k / 32;
   // output rows start 16-byte aligned: the staged epilogue's 16-byte stores
-  const bool y_st = ((uintptr_t)g.y % 16) == 0 && ((g.ld_y * (BF16OUT ? 2 : 4)) % 16) == 0;
+  constexpr bool BF16OUT = OUT == 1;
+  const bool y_st = OUT == 2 || (((uintptr_t)g.y % 16) == 0 && ((g.ld_y * (BF16OUT ? 2 : 4)) % 16) == 0);
 
   // ---- direct LDS load plan: the first half of the waves loads weight rows,
   // the second half activation rows; wave w fills stage rows
@@ -341,6 +344,72 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
     // ---- epilogue of this workgroup's j-th tile
     int tm, tn;
     tile_coords(j * grid + slot, tiles_m, tiles_n, tm, tn);
+    if constexpr (OUT == 2) {
+      // MXFP4 output, straight from the accumulators.  Fragment a of a wave
+      // covers one 32-block along N for each of its 32 rows: lane l (row
+      // l % 32, lane group g = l / 32) holds the runs n = 8 t + 4 g .. + 3,
+      // t = 0..3, so the block's other half is in lane l ^ 32.  Block amax:
+      // the lane's 16 values, then the partner's (exact); the E8M0 rule and
+      // the E2M1 converter as in the quantizer.  One 32-bit exchange then
+      // gives lane group 0 the block's code bytes 0..7 and group 1 bytes
+      // 8..15, stored as 8 contiguous bytes per lane.
+      // the wave's 128 columns start on a 128-column (tiled stage) boundary:
+      // fragment a is block a of that stage, at chunk a ^ swz(row) (tiled)
+      // or 16 a bytes further along the row (row-major)
+      const int nw0 = tn * BN + wn * (BN / WN);
+#pragma unroll
+      for (int bb = 0; bb < FM; ++bb) {
+        const int m = tm * BM + wm * (BM / WM) + 32 * bb + lr;
+        uint8_t* cbase;
+        uint8_t* sbase;
+        int swr = 0;
+        if (g.q_tiled) {
+          const uint32_t r8 = (uint32_t)m & 255u;
+          const uint64_t ts = (uint64_t)((uint32_t)m >> 8) * ((uint32_t)g.n >> 7) + ((uint32_t)nw0 >> 7);
+          cbase = g.q_codes + ts * 16384 + r8 * 64;
+          sbase = g.q_scales + ts * 1024 + r8 * 4;
+          swr = swz((int)r8);
+        } else {
+          cbase = g.q_codes + (int64_t)m * (g.n >> 1) + (nw0 >> 1);
+          sbase = g.q_scales + (int64_t)m * (g.n >> 5) + (nw0 >> 5);
+        }
+        const bool row_ok = m < g.m;
+#pragma unroll
+        for (int a = 0; a < FN; ++a) {
+          float am = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(acc[a][bb][r]));
+          am = fmaxf(am, __shfl_xor(am, 32));
+          const uint32_t ef = __float_as_uint(am) >> 23;
+          const uint32_t sb = ef > 2u ? ef - 2u : 0u;
+          const float sc = __uint_as_float(sb ? sb << 23 : 0x00400000u);
+          uint32_t w0 = 0, w1 = 0;   // runs t = 0, 1 and t = 2, 3: two code bytes per run
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, acc[a][bb][0], acc[a][bb][1], sc, 0);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, acc[a][bb][2], acc[a][bb][3], sc, 1);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, acc[a][bb][4], acc[a][bb][5], sc, 2);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, acc[a][bb][6], acc[a][bb][7], sc, 3);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, acc[a][bb][8], acc[a][bb][9], sc, 0);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, acc[a][bb][10], acc[a][bb][11], sc, 1);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, acc[a][bb][12], acc[a][bb][13], sc, 2);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, acc[a][bb][14], acc[a][bb][15], sc, 3);
+          // group 0 keeps w0 (bytes 0-1, 4-5) and takes the partner's w0
+          // (bytes 2-3, 6-7); group 1 keeps w1 (bytes 10-11, 14-15) and
+          // takes the partner's w1 (bytes 8-9, 12-13)
+          const uint32_t recv = (uint32_t)__shfl_xor((int)(lg ? w0 : w1), 32);
+          const uint32_t lo = lg ? recv : w0, hi = lg ? w1 : recv;
+          const uint32_t d0 = (lo & 0xFFFFu) | (hi << 16), d1 = (lo >> 16) | (hi & 0xFFFF0000u);
+          if (row_ok && nw0 + 32 * a < g.n) {
+            const int chunk = g.q_tiled ? (a ^ swr) : a;
+            *reinterpret_cast<uint2*>(cbase + 16 * chunk + 8 * lg) = make_uint2(d0, d1);
+            if (lg == 0) sbase[a] = (uint8_t)sb;
+          }
+          // one fragment at a time: keeps the accumulator reads from being
+          // hoisted together (register pressure)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      continue;
+    }
     if constexpr (WN == 2 && WM == 2) {
       // Interior tiles: stage each wave's 128 x 128 output block through the
       // ring slot of the stage just computed (free until the next issue,
@@ -387,6 +456,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
         continue;
       }
     }
+    if constexpr (OUT != 2) {
 #pragma unroll
     for (int bb = 0; bb < FM; ++bb) {
       const int m = tm * BM + wm * (BM / WM) + 32 * bb + lr;
@@ -423,6 +493,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
         }
       }
     }
+    }
   }
   // no direct LDS load may still be writing when the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(0);
@@ -445,7 +516,8 @@ int cu_count() {
 bool gemm_large_supported(const GemmArgs& g) {
   const int64_t m = (g.m + BM - 1) / BM * BM, n = (g.n + BN - 1) / BN * BN;   // padded rows
   return (g.k % KS) == 0 && ((uintptr_t)g.a_scales % 4) == 0 && ((uintptr_t)g.b_scales % 4) == 0 &&
-         m * (g.k / 2) < (int64_t(1) << 32) && n * (g.k / 2) < (int64_t(1) << 32);
+         m * (g.k / 2) < (int64_t(1) << 32) && n * (g.k / 2) < (int64_t(1) << 32) &&
+         (!g.q_out || (g.n % (g.q_tiled ? 128 : 32)) == 0);
 }
 
 hipError_t launch_gemm_large(const GemmArgs& g, hipStream_t s) {
@@ -456,10 +528,12 @@ hipError_t launch_gemm_large(const GemmArgs& g, hipStream_t s) {
   const int xcd_remap = (grid % 8) == 0;
   const size_t ybytes = g.y_bf16 ? 2 : 4;
   const int y_vec = (((uintptr_t)g.y) % (4 * ybytes) == 0) && (g.ld_y % 4 == 0);
-  if (g.y_bf16)
-    gemm_large_kernel<true><<<grid, NT, 0, s>>>(g, tiles_m, tiles_n, grid, xcd_remap, y_vec);
+  if (g.q_out)
+    gemm_large_kernel<2><<<grid, NT, 0, s>>>(g, tiles_m, tiles_n, grid, xcd_remap, y_vec);
+  else if (g.y_bf16)
+    gemm_large_kernel<1><<<grid, NT, 0, s>>>(g, tiles_m, tiles_n, grid, xcd_remap, y_vec);
   else
-    gemm_large_kernel<false><<<grid, NT, 0, s>>>(g, tiles_m, tiles_n, grid, xcd_remap, y_vec);
+    gemm_large_kernel<0><<<grid, NT, 0, s>>>(g, tiles_m, tiles_n, grid, xcd_remap, y_vec);
   return hipGetLastError();
 }
 

@@ -37,6 +37,13 @@ struct GemmArgs {
   int64_t ld_y;
   bool y_bf16;
   bool tiled;               // both operands in MXFP4_LAYOUT_TILED
+  // MXFP4 output (large-tile kernel only; n % 32 == 0, n % 128 == 0 when
+  // q_tiled): Y requantized per 32-block along N into q_codes / q_scales
+  // (y unused)
+  bool q_out = false;
+  bool q_tiled = false;     // output in MXFP4_LAYOUT_TILED
+  uint8_t* q_codes = nullptr;
+  uint8_t* q_scales = nullptr;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);

@@ -158,6 +158,23 @@ def test_linear_small_argument_errors():
     assert ls(A, BF, 4, 64, 64, ctypes.byref(kr), A, A, 8, R, A, F, 8, None) == INV   # p*q != 32
 
 
+def test_gemm_requant_argument_errors():
+    INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
+    A, R, T = ALIGNED, mx.ROWMAJOR, mx.TILED
+    gq = mx.lib().mxfp4_gemm_requant
+    assert gq(A, A, 4, A, A, 256, 128, 2, A, A, R, None) == INV       # bad operand layout
+    assert gq(A, A, 4, A, A, 256, 128, R, A, A, 5, None) == INV       # bad output layout
+    assert gq(A, A, 4, A, A, 256, 48, R, A, A, R, None) == INV        # k % 32
+    assert gq(A, A, -1, A, A, 256, 128, R, A, A, R, None) == INV
+    assert gq(A, A, 4, A, A, 256, 128, R, NULL, A, R, None) == INV
+    assert gq(NULL, NULL, 0, NULL, NULL, 256, 128, R, NULL, NULL, R, None) == OK   # m == 0
+    assert gq(A, A, 4, A, A, 200, 128, R, A, A, R, None) == UNS       # n % 32
+    assert gq(A, A, 4, A, A, 160, 128, R, A, A, T, None) == UNS       # tiled output: n % 128
+    assert gq(A, A, 4, A, A, 256, 96, R, A, A, R, None) == UNS        # k % 128
+    assert gq(A, A, 4, A, A, 256, 128, R, A + 8, A, R, None) == UNS   # codes not 16 B aligned
+    assert gq(A, A, 4, A, A, 256, 128, R, A, A + 1, T, None) == UNS   # scales not 4 B aligned
+
+
 def test_tiled_bytes():
     INV = mx.MXFP4_ERR_INVALID_ARG
     assert mx.tiled_bytes(1, 128) == (256 * 64, 256 * 4)
