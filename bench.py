@@ -364,7 +364,7 @@ def main():
     y_bytes = m * n * (2 if wl.out_dtype == "bf16" else 4)
     g_bytes = (m + n) * (k // 2 + k // 32) + y_bytes
     small_m = m <= 64        # decode shapes run the small-M kernel, bound by streaming W from HBM
-    g_src = ("gemm.hip", "gemm_small.hip", "internal.h") if small_m else ("gemm.hip", "gemm_large.hip", "internal.h")
+    g_src = ("gemm.hip", "gemm_small.hip", "block_quant.h", "internal.h") if small_m else ("gemm.hip", "gemm_large.hip", "internal.h")
     traffic = recorded_traffic("gemm", args.workload, source_digest(*g_src))
     q_traffic = recorded_traffic("quantize", args.workload, source_digest("quantize.hip", "block_quant.h", "internal.h"))
     if small_m:
