@@ -10,14 +10,18 @@ before the timed region; the step cycles through enough buffer sets (X, W,
 codes, scales, Y) that the working set exceeds the 256 MB Infinity Cache.
 
 Prints one JSON line:
-  value       2*M*N*K / (time of one step), TFLOP/s.  A step is one quantize +
-              GEMM.  For decode shapes (M <= 64, bf16 activations) both that
-              and one launch of the fused layer (mxfp4_linear_small) are
-              timed; the faster is the step (config.path) and the other is
-              reported beside it (`split` or `fused`)
+  value       2*M*N*K / (time of one step), TFLOP/s, from HIP events around
+              the whole loop of K steps (no event markers between launches).
+              A step is one quantize + GEMM.  For decode shapes (M <= 64,
+              bf16 activations) both that and one launch of the fused layer
+              (mxfp4_linear_small) are timed; the faster is the step
+              (config.path) and the other is reported beside it (`split` or
+              `fused`)
   roofline    the dominant kernel (the GEMM, or the fused layer for decode
               shapes, bytes = bf16 X + MXFP4 W + Y), timed by HIP events
-              recorded around every launch in the timed region.  Large M: the
+              recorded around every launch of a second loop of the same K
+              steps (markers between launches delay the next launch, so that
+              loop's total is not the step time).  Large M: the
               MFMA-bound large-tile kernel, algorithmic FLOPs per launch / its
               mean launch time, against the dense MXFP4 MFMA peak.  M <= 64
               (decode): the HBM-bound small-M kernel, algorithmic bytes (both
@@ -179,14 +183,20 @@ def gpu_leg(name: str, steps: int, warmup: int):
 
     stream = torch.cuda.current_stream(dev)   # the stream every launch goes to
 
-    def time_loop(parts):
-        """Time `steps` steps; HIP events on the launch stream around every
-        part of every step, and around the whole loop."""
+    def time_loop(parts, marks):
+        """Time `steps` steps with HIP events on the launch stream around the
+        whole loop; with `marks`, also around every part of every step.  An
+        event marker between two launches makes the command processor finish
+        the first before it stamps the time, which removes the overlap of one
+        launch's start with the previous one's end: the step time comes from a
+        loop without them, the per-launch durations from a second loop with
+        them."""
         for i in range(warmup):
             for f in parts:
                 f(sets[i % nsets])
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(steps)] \
+            if marks else None
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -194,21 +204,27 @@ def gpu_leg(name: str, steps: int, warmup: int):
         t0.record(stream)
         for i in range(steps):
             s = sets[i % nsets]
-            e = ev[i]
-            e[0].record(stream)
-            for j, f in enumerate(parts):
-                f(s)
-                e[j + 1].record(stream)
+            if marks:
+                e = ev[i]
+                e[0].record(stream)
+                for j, f in enumerate(parts):
+                    f(s)
+                    e[j + 1].record(stream)
+            else:
+                for f in parts:
+                    f(s)
         t1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        per = [np.array([e[j].elapsed_time(e[j + 1]) for e in ev]) for j in range(len(parts))]
+        per = [np.array([e[j].elapsed_time(e[j + 1]) for e in ev]) for j in range(len(parts))] if marks else None
         return t0.elapsed_time(t1), wall, per
 
-    total_ms, wall, (q_ms, g_ms) = time_loop(split)
+    total_ms, wall, _ = time_loop(split, False)
+    _, _, (q_ms, g_ms) = time_loop(split, True)
     fused_res = None
     if use_fused:
-        f_total, f_wall, (f_ms,) = time_loop(fused)
+        f_total, f_wall, _ = time_loop(fused, False)
+        _, _, (f_ms,) = time_loop(fused, True)
         fused_res = dict(total_ms=f_total, wall_s=f_wall, ms=f_ms)
 
     # --- the transforms side by side on this workload's activations: the
