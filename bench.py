@@ -14,9 +14,12 @@ Prints one JSON line:
               the whole loop of K steps (no event markers between launches).
               A step is one quantize + GEMM.  For decode shapes (M <= 64,
               bf16 activations) both that and one launch of the fused layer
-              (mxfp4_linear_small) are timed; the faster is the step
-              (config.path) and the other is reported beside it (`split` or
-              `fused`)
+              (mxfp4_linear_small) are timed.  Each path is timed launched
+              eagerly and replayed from HIP graphs (one captured step per
+              buffer set: the same kernels, without the host-side launch
+              cost); the fastest is the step (config.path, config.launch),
+              all four are in `launch`, and the other path is reported beside
+              it (`split` or `fused`)
   roofline    the dominant kernel (the GEMM, or the fused layer for decode
               shapes, bytes = bf16 X + MXFP4 W + Y), timed by HIP events
               recorded around every launch of a second loop of the same K
@@ -227,6 +230,30 @@ def gpu_leg(name: str, steps: int, warmup: int):
         _, _, (f_ms,) = time_loop(fused, True)
         fused_res = dict(total_ms=f_total, wall_s=f_wall, ms=f_ms)
 
+    # The same steps replayed from HIP graphs, one per buffer set: the
+    # launches are recorded once, so a step carries no host-side launch cost
+    # (small steps are otherwise bound by it).  The captured work is the
+    # eager step's, kernel for kernel.
+    def capture(parts, key):
+        for s in sets:
+            for f in parts:
+                f(s)
+        torch.cuda.synchronize()
+        for s in sets:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for f in parts:
+                    f(s)
+            s[key] = gr
+        torch.cuda.synchronize()
+
+    graph_ms = {}
+    capture(split, "graph_split")
+    graph_ms["quantize+gemm"], _, _ = time_loop([lambda s: s["graph_split"].replay()], False)
+    if use_fused:
+        capture(fused, "graph_fused")
+        graph_ms["fused"], _, _ = time_loop([lambda s: s["graph_fused"].replay()], False)
+
     # --- the transforms side by side on this workload's activations: the
     # quantizer alone (the GEMM does not depend on the transform)
     def time_parts(fn, reps=50):
@@ -306,7 +333,10 @@ def gpu_leg(name: str, steps: int, warmup: int):
     del src, dst
 
     props = torch.cuda.get_device_properties(dev)
-    return dict(m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms,
+    for s in sets:
+        s.pop("graph_split", None)
+        s.pop("graph_fused", None)
+    return dict(m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms, graph_ms=graph_ms,
                 fused=fused_res, copy_gbps=copy_gbps, transforms=transforms, wfit=wfit, requant=requant_ms, nsets=nsets, device=props.name,
                 cus=props.multi_processor_count, arch=getattr(props, "gcnArchName", ""))
 
@@ -370,7 +400,17 @@ def main():
     g = gpu_leg(args.workload, args.steps, args.warmup)
     m, n, k, wl = g["m"], g["n"], g["k"], g["wl"]
     flops = 2.0 * m * n * k
-    ms_step = g["total_ms"] / args.steps
+    # the step: the fastest of the two-launch path and the fused layer, each
+    # launched eagerly or replayed from HIP graphs
+    cands = {("quantize+gemm", "eager"): g["total_ms"], ("quantize+gemm", "graph"): g["graph_ms"]["quantize+gemm"]}
+    if g["fused"] is not None:
+        cands[("fused", "eager")] = g["fused"]["total_ms"]
+        cands[("fused", "graph")] = g["graph_ms"]["fused"]
+    best_path, best_launch = min(cands, key=cands.get)
+    ms_step = cands[(best_path, best_launch)] / args.steps
+    per_path = {}
+    for (p, lch), v in cands.items():
+        per_path.setdefault(p, {})[lch] = round(v / args.steps, 5)
     g_us = float(np.mean(g["g_ms"])) * 1e3
     q_us = float(np.mean(g["q_ms"])) * 1e3
     g_tflops = flops / (g_us * 1e-6) / 1e12
@@ -393,19 +433,17 @@ def main():
     roof.update({"traffic": traffic, "us_per_launch": round(g_us, 2),
                  "us_min": round(float(np.min(g["g_ms"])) * 1e3, 2), "algorithmic_bytes": g_bytes,
                  "algorithmic_flops": flops})
-    split_info = {"ms_per_step": round(ms_step, 5), "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2)}
+    split_info = {"ms_per_step": per_path["quantize+gemm"], "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2)}
     fz = g["fused"]
-    if fz is not None and fz["total_ms"] > g["total_ms"]:
-        # the two-launch path was faster for this workload: it is the step, the fused figures are reported
-        split_info = None
-        fused_only = {"ms_per_step": round(fz["total_ms"] / args.steps, 5),
-                      "us_per_launch": round(float(np.mean(fz["ms"])) * 1e3, 2)}
+    if best_path != "fused":
+        # the two-launch path is the step; the fused figures, if any, are reported beside it
+        fused_only = None if fz is None else {"ms_per_step": per_path["fused"],
+                                              "us_per_launch": round(float(np.mean(fz["ms"])) * 1e3, 2)}
         fz = None
     else:
         fused_only = None
     if fz is not None:
         # the step is the fused layer: one launch reads bf16 X and the MXFP4 weights, writes Y
-        ms_step = fz["total_ms"] / args.steps
         f_us = float(np.mean(fz["ms"])) * 1e3
         f_bytes = x_bytes + n * (k // 2 + k // 32) + y_bytes
         f_gbps = f_bytes / (f_us * 1e-6) / 1e9
@@ -434,7 +472,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "m": m, "n": n, "k": k, "x_dtype": wl.x_dtype,
                    "rotation": wl.rot or "none", "out_dtype": wl.out_dtype, "layout": "tiled",
-                   "path": "fused" if fz is not None else "quantize+gemm",
+                   "path": best_path, "launch": best_launch,
                    "buffer_sets": g["nsets"], "parallelism": "single-gpu"},
         "roofline": roof,
         "quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
@@ -444,6 +482,7 @@ def main():
                      "algorithmic_bytes": q_bytes},
         "split": split_info if fz is not None else None,
         "fused": fused_only,
+        "launch": per_path,
         "transforms": {t: {"quantize_us": round(v * 1e3, 2),
                            "quantize_gbps": round(q_bytes / (v * 1e-3) / 1e9, 1),
                            "step_us": round(v * 1e3 + g_us, 2)} for t, v in g["transforms"].items()},
