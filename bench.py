@@ -43,6 +43,9 @@ Prints one JSON line:
               per 32-block in the epilogue) beside the bf16-output GEMM, both
               timed back to back over the buffer sets
   copy_gbps   a plain device copy in the same run (practical HBM ceiling)
+  mfma_ceiling  the scaled FP4 MFMA alone, every SIMD issuing back to back
+              with no memory traffic (libmxfp4_ceiling.so): TFLOP/s, the
+              engine clock it held, and the GEMM's rate as a fraction of it
   cpu_baseline  the CPU oracle on the same workload (all rows by default)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -336,9 +339,50 @@ def gpu_leg(name: str, steps: int, warmup: int):
     for s in sets:
         s.pop("graph_split", None)
         s.pop("graph_fused", None)
-    return dict(m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms, graph_ms=graph_ms,
+    ceiling = mfma_ceiling(dev, stream, props.multi_processor_count)
+    return dict(ceiling=ceiling, m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms, graph_ms=graph_ms,
                 fused=fused_res, copy_gbps=copy_gbps, transforms=transforms, wfit=wfit, requant=requant_ms, nsets=nsets, device=props.name,
                 cus=props.multi_processor_count, arch=getattr(props, "gcnArchName", ""))
+
+
+def mfma_ceiling(dev, stream, cus: int):
+    """The block-scaled FP4 MFMA alone (libmxfp4_ceiling.so): one workgroup
+    per CU, every SIMD issuing independent MFMAs back to back, no memory
+    traffic.  Returns its TFLOP/s after a warm-up long enough for the clock to
+    settle, and the engine clock it ran at (wave cycles / launch time)."""
+    import ctypes
+
+    import torch
+    from mxfp4_w4a4_quantized_amd import build as hip_build
+    if not os.path.exists(hip_build.CEILING_LIB):
+        raise RuntimeError(f"{hip_build.CEILING_LIB} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(hip_build.CEILING_LIB)
+    L.mxfp4_ceiling_mfma.restype = ctypes.c_int
+    L.mxfp4_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    iters = 4096
+    out = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    cyc = torch.zeros(cus * 4, dtype=torch.int64, device=dev)
+
+    def launch():
+        st = L.mxfp4_ceiling_mfma(cus, iters, out.data_ptr(), cyc.data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"mxfp4_ceiling_mfma failed: HIP error {st}")
+
+    for _ in range(20):
+        launch()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s_per = e0.elapsed_time(e1) * 1e-3 / reps
+    flops = 2.0 * 32 * 32 * 64 * 8 * iters * 4 * cus
+    clock = float(cyc.double().mean()) / s_per / 1e9
+    return dict(tflops=flops / s_per / 1e12, clock_ghz=clock)
 
 
 # ----------------------------------------------------------------- CPU leg ---
@@ -494,6 +538,10 @@ def main():
             "same_gemm_bf16_out_us": round(g["requant"][1] * 1e3, 2),
             "y_bytes": m * (n // 2 + n // 32), "y_bytes_bf16": m * n * 2},
         "copy_gbps": round(g["copy_gbps"], 1),
+        "mfma_ceiling": {"tflops": round(g["ceiling"]["tflops"], 1),
+                         "frac_of_peak": round(g["ceiling"]["tflops"] / PEAK_MXFP4_TFLOPS, 4),
+                         "clock_ghz": round(g["ceiling"]["clock_ghz"], 3),
+                         "gemm_frac_of_ceiling": None if small_m else round(g_tflops / g["ceiling"]["tflops"], 4)},
         "device": {"name": g["device"], "arch": g["arch"], "cus": g["cus"]},
     }
     if args.cpu_rows != 0:

@@ -1,7 +1,8 @@
 """Build step for the HIP library ``libmxfp4.so`` (gfx950 only).
 
 Compiles the kernels and the C-ABI layer in ``csrc/`` with hipcc into a shared
-library next to this file.  Flags:
+library next to this file, and the benchmark's MFMA-rate measurement kernel
+(``csrc/ceiling.hip``) into ``libmxfp4_ceiling.so``.  Flags:
   --offload-arch=gfx950          CDNA4 only
   -ffp-contract=off              no implicit fused multiply-adds: the quantizer's
                                  fp32 results follow the written op order
@@ -17,6 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmxfp4.so")
+CEILING_LIB = os.path.join(HERE, "libmxfp4_ceiling.so")
 SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemm_large.hip", "gemm_small.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -58,6 +60,15 @@ def build(verbose: bool = False, jobs: int = 3) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    # the measurement kernel, a library of its own (not part of the MXFP4 ABI)
+    cmd = [HIPCC] + FLAGS + ["-shared", os.path.join(CSRC, "ceiling.hip"), "-o", CEILING_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        print(r.stdout.decode(errors="replace"), file=sys.stderr)
+        raise RuntimeError("hipcc failed for ceiling.hip")
+    os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
     return LIB
 
 

@@ -1,0 +1,85 @@
+// Measurement kernel, not part of the MXFP4 path: the rate at which this
+// device sustains the block-scaled FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4,
+// E2M1 operands, one E8M0 byte per 32-element block, as the large GEMM issues
+// it) when every SIMD of every CU issues it back to back, with no memory
+// traffic at all.  The dense FP4 peak assumes the peak engine clock; under
+// this load the clock the device holds is lower, and this kernel measures
+// what that leaves.  The benchmark reports it beside the GEMM's roofline.
+//
+// One workgroup of four waves per CU (one wave per SIMD, as the GEMM).  Each
+// wave keeps 8 independent accumulators (no MFMA waits on another's result)
+// and cycles through 4 A and 4 B operand registers filled with pseudo-random
+// codes and per-MFMA scale bytes, so the operands toggle like real data.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t mix(uint32_t x) {   // 32-bit integer hash (xorshift-multiply)
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ __launch_bounds__(256, 1) void mfma_loop(float* out, unsigned long long* cycles, int iters, uint32_t seed) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t base = seed * 0x9e3779b9u + (blockIdx.x * 256u + threadIdx.x) * 64u;
+  v8i a[4], b[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {   // FP4 operands use the first 4 registers
+      a[s][i] = i < 4 ? (int)mix(base + 8 * s + i) : 0;
+      b[s][i] = i < 4 ? (int)mix(base + 32 + 8 * s + i) : 0;
+    }
+  uint32_t sa[8], sb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {   // scale bytes 120..135 in all four byte lanes
+    sa[j] = 0x78787878u + (mix(base + 100 + j) & 0x0f0f0f0fu);
+    sb[j] = 0x78787878u + (mix(base + 200 + j) & 0x0f0f0f0fu);
+  }
+  v16f acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 3], b[(j + u) & 3], acc[j], 4, 4, 0,
+                                                                 (int)sa[j], 1, (int)sb[7 - j]);
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[j][r];
+  out[blockIdx.x * 256 + threadIdx.x] = sum;
+  if (lane == 0) cycles[blockIdx.x * 4 + wave] = (unsigned long long)(t1 - t0);
+}
+
+}  // namespace
+
+// blocks workgroups (use the CU count), iters rounds of 8 MFMAs per wave (a
+// multiple of 4).
+// out: blocks * 256 floats, cycles: blocks * 4 counters (device memory); the
+// launch goes to `stream`.  Returns 0, or the HIP error code of the launch.
+extern "C" __attribute__((visibility("default"))) int mxfp4_ceiling_mfma(int blocks, int iters, float* out,
+                                                                           unsigned long long* cycles, void* stream) {
+  if (blocks <= 0 || iters <= 0 || iters % 4 != 0 || out == nullptr || cycles == nullptr)
+    return (int)hipErrorInvalidValue;
+  mfma_loop<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(out, cycles, iters, 12345u);
+  return (int)hipGetLastError();
+}

@@ -231,3 +231,17 @@ def test_inverse_transpose_errors():
     assert mx.lib().mxfp4_inverse_transpose(None, 4, None) == mx.MXFP4_ERR_INVALID_ARG
     m = np.eye(4, dtype=np.float32)
     assert mx.lib().mxfp4_inverse_transpose(m.ctypes.data, 33, m.ctypes.data) == mx.MXFP4_ERR_INVALID_ARG
+
+
+def test_measurement_library_loads_and_rejects_bad_arguments():
+    # the benchmark's MFMA-rate kernel ships as a library of its own, outside
+    # the MXFP4 ABI; argument errors return before any device call
+    from mxfp4_w4a4_quantized_amd import build as hip_build
+    L = ctypes.CDLL(hip_build.CEILING_LIB)
+    out = os.popen(f"nm -D --defined-only {hip_build.CEILING_LIB}").read()
+    assert set(re.findall(r"\bT (\w+)", out)) == {"mxfp4_ceiling_mfma"}
+    L.mxfp4_ceiling_mfma.restype = ctypes.c_int
+    L.mxfp4_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    for blocks, iters, o, c in ((0, 4, ALIGNED, ALIGNED), (4, 0, ALIGNED, ALIGNED), (4, 6, ALIGNED, ALIGNED),
+                                (4, 4, NULL, ALIGNED), (4, 4, ALIGNED, NULL)):
+        assert L.mxfp4_ceiling_mfma(blocks, iters, o, c, NULL) != 0
