@@ -355,7 +355,7 @@ def mfma_ceiling(dev, stream, cus: int):
     import torch
     from mxfp4_w4a4_quantized_amd import build as hip_build
     if not os.path.exists(hip_build.CEILING_LIB):
-        raise RuntimeError(f"{hip_build.CEILING_LIB} is missing: build it with __graft_entry__.build()")
+        raise RuntimeError(f"{hip_build.CEILING_LIB} is missing: build it with python -m mxfp4_w4a4_quantized_amd.build")
     L = ctypes.CDLL(hip_build.CEILING_LIB)
     L.mxfp4_ceiling_mfma.restype = ctypes.c_int
     L.mxfp4_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]

@@ -71,7 +71,7 @@ def lib() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m mxfp4_w4a4_quantized_amd.build "
                            "(the MXFP4 path has no CPU fallback)")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64

@@ -36,9 +36,10 @@
 //    ((row >> 1) ^ (row >> 2)) & 3, so every 16-lane phase of a fragment's
 //    ds_read_b128 hits 16 distinct 16-byte bank groups of the 64-bank LDS.
 //  * Fragments are double-buffered in registers: the second sub-step's
-//    fragments load while the first sub-step's MFMAs run, and the barrier
-//    sits between the two sub-steps, so the next stage's first fragments load
-//    while the second sub-step's MFMAs run.
+//    fragments load while the first sub-step's MFMAs run, and the next
+//    stage's scales and first fragments load while the second sub-step's
+//    MFMAs run.  The stage's barrier therefore sits before its first
+//    sub-step, where it also certifies the next stage's arrival.
 //  * Tiles are ordered in groups of 4 M-tiles (N fastest within a group),
 //    and workgroup b, which the dispatcher places on XCD b % 8, takes logical
 //    tiles so that the 32 workgroups of one XCD work on one compact 4 x 8
