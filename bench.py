@@ -33,6 +33,8 @@ Prints one JSON line:
               counters (profiles/), or null if the kernel source changed since
   quantize    the quantizer kernel: algorithmic bytes (X read, codes and
               scales written) per launch / its mean launch time, against HBM
+              and against the device copy measured in the same run
+              (frac_of_copy); mean, median and min per launch
   transforms  the quantizer on the same activations with each block transform
               (none, Hadamard-32, Kronecker 4x8, per-channel smoothing), and
               the step time with the same GEMM
@@ -470,11 +472,13 @@ def main():
     if small_m:
         g_gbps = g_bytes / (g_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(g_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(g_gbps / PEAK_HBM_GBPS, 4), "kernel": "gemm_small"}
+                "frac": round(g_gbps / PEAK_HBM_GBPS, 4), "frac_of_copy": round(g_gbps / g["copy_gbps"], 4),
+                "kernel": "gemm_small"}
     else:
         roof = {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_MXFP4_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_MXFP4_TFLOPS, 4), "kernel": "gemm_large"}
     roof.update({"traffic": traffic, "us_per_launch": round(g_us, 2),
+                 "us_median": round(float(np.median(g["g_ms"])) * 1e3, 2),
                  "us_min": round(float(np.min(g["g_ms"])) * 1e3, 2), "algorithmic_bytes": g_bytes,
                  "algorithmic_flops": flops})
     split_info = {"ms_per_step": per_path["quantize+gemm"], "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2)}
@@ -495,8 +499,10 @@ def main():
                                      source_digest("gemm_small.hip", "block_quant.h", "internal.h"))
         split_info["gemm_roofline"] = roof
         roof = {"bound": "hbm", "achieved": round(f_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(f_gbps / PEAK_HBM_GBPS, 4), "kernel": "linear_small", "traffic": f_traffic,
-                "us_per_launch": round(f_us, 2), "us_min": round(float(np.min(fz["ms"])) * 1e3, 2),
+                "frac": round(f_gbps / PEAK_HBM_GBPS, 4), "frac_of_copy": round(f_gbps / g["copy_gbps"], 4),
+                "kernel": "linear_small", "traffic": f_traffic,
+                "us_per_launch": round(f_us, 2), "us_median": round(float(np.median(fz["ms"])) * 1e3, 2),
+                "us_min": round(float(np.min(fz["ms"])) * 1e3, 2),
                 "algorithmic_bytes": f_bytes, "algorithmic_flops": flops}
     metric = METRIC if args.workload == "flux_up" else \
         f"MXFP4 GEMM TFLOPS @ M={m},K={k},N={n} (% peak); quantize GB/s (% HBM)"
@@ -521,7 +527,9 @@ def main():
         "roofline": roof,
         "quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
+                     "frac_of_copy": round(q_gbps / g["copy_gbps"], 4),
                      "traffic": q_traffic, "us_per_launch": round(q_us, 2),
+                     "us_median": round(float(np.median(g["q_ms"])) * 1e3, 2),
                      "us_min": round(float(np.min(g["q_ms"])) * 1e3, 2),
                      "algorithmic_bytes": q_bytes},
         "split": split_info if fz is not None else None,
