@@ -52,6 +52,8 @@
 //    shapes to the general kernel).
 #include "internal.h"
 
+#include <atomic>
+
 #ifndef MXFP4_GEMM_WN
 #define MXFP4_GEMM_WN 2
 #define MXFP4_GEMM_WM 2
@@ -500,16 +502,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+// CU count of the current device, cached per device.  Calls may come from
+// several host threads at once: the cache slots are atomics (every writer
+// stores the same value).
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace
