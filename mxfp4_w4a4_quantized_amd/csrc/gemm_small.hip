@@ -31,8 +31,11 @@
 //    loads (each byte is used once per call); the activation fragments are
 //    shared by every workgroup and stay in L2.
 //  * Row-major operands: a wave's code load covers 16 rows x 64 contiguous
-//    bytes.  Tiled operands: one K step of 16 rows is one contiguous 1 KiB
-//    run.  Rows beyond M or N are clamped to a valid row (their results are
+//    bytes, and each lane loads its scale byte per step.  Tiled operands: one
+//    K step of 16 rows is one contiguous 1 KiB run, and the scales of 4 steps
+//    come in with one dword load per lane, spread to the lanes that use them
+//    by a cross-lane permute (a quarter of the scale load instructions; the
+//    scale loads were a third of the kernel's memory instructions).  Rows beyond M or N are clamped to a valid row (their results are
 //    never stored); blocks beyond K are zero codes with a zero scale byte, so
 //    a K tail contributes exactly 0.
 //  * M is covered in groups of 16 rows that reuse the weight fragments held
@@ -101,6 +104,7 @@ struct Operand {
   const uint8_t* code;
   const uint8_t* scale;
   int64_t cstride, sstride;
+  const uint8_t* scale_row;   // tiled: the row's 4 scale bytes of stage 0
 };
 
 template <bool TILED>
@@ -112,13 +116,15 @@ __device__ __forceinline__ Operand operand(const uint8_t* codes, const uint8_t* 
     const int64_t t = row >> 8;
     const int r = row & 255;
     o.code = codes + t * nstage * 16384 + r * 64 + 16 * (lg ^ tiled_swz(r));
-    o.scale = scales + t * nstage * 1024 + r * 4 + lg;
+    o.scale_row = scales + t * nstage * 1024 + r * 4;
+    o.scale = o.scale_row + lg;
     o.cstride = 16384;
     o.sstride = 1024;
   } else {
     const int64_t rr = row < rows ? row : rows - 1;
     o.code = codes + rr * (k >> 1) + 16 * lg;
     o.scale = scales + rr * (k >> 5) + lg;
+    o.scale_row = o.scale;
     o.cstride = 64;
     o.sstride = 4;
   }
@@ -131,9 +137,26 @@ __device__ __forceinline__ Operand operand_rt(bool tiled, const uint8_t* codes, 
   return tiled ? operand<true>(codes, scales, row, rows, k, lg) : operand<false>(codes, scales, row, rows, k, lg);
 }
 
+// Tiled operands: the scale bytes of one K step of a 16-row fragment are 64
+// contiguous bytes (row-major [16][4]).  Lane (r, g) loads the dword of row r
+// for step s0 + 4 i + g, i.e. the scales of all four blocks of that step; the
+// scale of step s0 + 4 i + j for the lane's own block g then sits in byte g of
+// lane (r, j)'s dword.  One dword load replaces four byte loads.
+template <int NCH>
+__device__ __forceinline__ void scales_dw(const Operand& o, int s0, int lane, int (&sc)[NCH]) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NCH / 4; ++i) {
+    const int dw = *reinterpret_cast<const int*>(o.scale_row + (int64_t)(s0 + 4 * i + lg) * o.sstride);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[4 * i + j] = __shfl(dw, 16 * j + lr) >> (8 * lg);
+  }
+}
+
 template <int MG, int NG, bool BF16OUT, bool TILED>
 __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int spw, int y_vec) {
   static_assert(MG * NG <= MAXACC, "reduction buffer holds MAXACC tiles per wave");
+  static_assert(CH % 4 == 0, "dword scale loads cover 4 steps");
   __shared__ v4f red[MAXW][MAXACC][64];
 
   const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
@@ -169,8 +192,12 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
           wf[q][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[q].code + (s0 + j) * w[q].cstride));
-          ws[q][j] = w[q].scale[(s0 + j) * w[q].sstride];
+          if constexpr (!TILED) ws[q][j] = w[q].scale[(s0 + j) * w[q].sstride];
         }
+      if constexpr (TILED) {
+#pragma unroll
+        for (int q = 0; q < NG; ++q) scales_dw<CH>(w[q], s0, lane, ws[q]);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < CH; ++j)
@@ -193,8 +220,9 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
           xf[j] = *reinterpret_cast<const u32x4*>(x[mg].code + (s0 + j) * x[mg].cstride);
-          xs[j] = x[mg].scale[(s0 + j) * x[mg].sstride];
+          if constexpr (!TILED) xs[j] = x[mg].scale[(s0 + j) * x[mg].sstride];
         }
+        if constexpr (TILED) scales_dw<CH>(x[mg], s0, lane, xs);
       } else {
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
@@ -341,6 +369,7 @@ __device__ __forceinline__ void quantize_raw(const RawBlock<XBF16>& b, const flo
 template <int MG, int NG, bool XBF16, int ROT, int P, int Q>
 __global__ __launch_bounds__(64 * MAXW) void linear_small_kernel(LinearArgs L, int spw, int y_vec) {
   static_assert(MG * NG <= MAXACC, "reduction buffer holds MAXACC tiles per wave");
+  static_assert(KC % 4 == 0, "dword scale loads cover 4 steps");
   __shared__ v4f red[MAXW][MAXACC][64];
   const GemmArgs& g = L.g;
 
@@ -389,6 +418,10 @@ __global__ __launch_bounds__(64 * MAXW) void linear_small_kernel(LinearArgs L, i
         load_block<XBF16>(xrow[mg] + (int64_t)col * 32 * esz, ok, raw[j]);
       }
       if (mg == 0) {
+        // tiled weights with the whole chunk inside this wave's range: one
+        // scale dword per weight group instead of KC scale bytes (not with
+        // the Kronecker and smoothing transforms, whose registers are full)
+        const bool dws = ROT <= 1 && g.tiled && s0 + KC <= s_end;
 #pragma unroll
         for (int j = 0; j < KC; ++j)
 #pragma unroll
@@ -398,9 +431,13 @@ __global__ __launch_bounds__(64 * MAXW) void linear_small_kernel(LinearArgs L, i
             ws[q][j] = 0;
             if (s < s_end && (g.tiled || 4 * s + lg < kblocks)) {
               wf[q][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[q].code + s * w[q].cstride));
-              ws[q][j] = w[q].scale[s * w[q].sstride];
+              if (!dws) ws[q][j] = w[q].scale[s * w[q].sstride];
             }
           }
+        if (dws) {
+#pragma unroll
+          for (int q = 0; q < NG; ++q) scales_dw<KC>(w[q], s0, lane, ws[q]);
+        }
       }
       u32x4 xf[KC];
       int xs[KC];
