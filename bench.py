@@ -15,16 +15,18 @@ Prints one JSON line:
               A step is one quantize + GEMM.  For decode shapes (M <= 64,
               bf16 activations) both that and one launch of the fused layer
               (mxfp4_linear_small) are timed.  Each path is timed launched
-              eagerly and replayed from HIP graphs (one captured step per
-              buffer set: the same kernels, without the host-side launch
-              cost); the fastest is the step (config.path, config.launch),
+              eagerly and replayed from HIP graphs (one graph per cycle of
+              steps over the buffer sets: the same kernels, with one host
+              launch per cycle); the fastest is the step (config.path, config.launch),
               all four are in `launch`, and the other path is reported beside
               it (`split` or `fused`)
   roofline    the dominant kernel (the GEMM, or the fused layer for decode
-              shapes, bytes = bf16 X + MXFP4 W + Y), timed by HIP events
-              recorded around every launch of a second loop of the same K
-              steps (markers between launches delay the next launch, so that
-              loop's total is not the step time).  Large M: the
+              shapes, bytes = bf16 X + MXFP4 W + Y), its launch time the mean
+              over K launches of that kernel alone, back to back over the
+              buffer sets and replayed from a HIP graph, with HIP events on
+              the launch stream around the loop.  `us_marked` gives the mean, median and min of a loop of
+              the K steps with events around every launch (each marker adds a
+              dispatch gap, which inflates short kernels).  Large M: the
               MFMA-bound large-tile kernel, algorithmic FLOPs per launch / its
               mean launch time, against the dense MXFP4 MFMA peak.  M <= 64
               (decode): the HBM-bound small-M kernel, algorithmic bytes (both
@@ -34,7 +36,7 @@ Prints one JSON line:
   quantize    the quantizer kernel: algorithmic bytes (X read, codes and
               scales written) per launch / its mean launch time, against HBM
               and against the device copy measured in the same run
-              (frac_of_copy); mean, median and min per launch
+              (frac_of_copy); launch time and `us_marked` as for roofline
   transforms  the quantizer on the same activations with each block transform
               (none, Hadamard-32, Kronecker 4x8, per-channel smoothing), and
               the step time with the same GEMM
@@ -235,29 +237,61 @@ def gpu_leg(name: str, steps: int, warmup: int):
         _, _, (f_ms,) = time_loop(fused, True)
         fused_res = dict(total_ms=f_total, wall_s=f_wall, ms=f_ms)
 
-    # The same steps replayed from HIP graphs, one per buffer set: the
-    # launches are recorded once, so a step carries no host-side launch cost
-    # (small steps are otherwise bound by it).  The captured work is the
-    # eager step's, kernel for kernel.
-    def capture(parts, key):
-        for s in sets:
+    # The same steps replayed from HIP graphs: one graph holds a whole cycle
+    # of steps, one per buffer set in order (a serving loop captures many
+    # layers the same way), so the host pays one graph launch per cycle
+    # instead of one launch per kernel; a second graph holds the first
+    # `steps % nsets` steps.  Exactly `steps` steps are timed, with events
+    # around the whole replay loop.  The captured work is the eager steps',
+    # kernel for kernel.
+    def capture(parts, count):
+        for s in sets[:count]:
             for f in parts:
                 f(s)
         torch.cuda.synchronize()
-        for s in sets:
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for s in sets[:count]:
                 for f in parts:
                     f(s)
-            s[key] = gr
         torch.cuda.synchronize()
+        return gr
 
-    graph_ms = {}
-    capture(split, "graph_split")
-    graph_ms["quantize+gemm"], _, _ = time_loop([lambda s: s["graph_split"].replay()], False)
+    def time_graph(parts):
+        cycle = capture(parts, nsets)
+        rest = steps % nsets
+        tail = capture(parts, rest) if rest else None
+        for _ in range(max(1, warmup // nsets)):
+            cycle.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps // nsets):
+            cycle.replay()
+        if tail is not None:
+            tail.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        del cycle, tail
+        return t0.elapsed_time(t1)
+
+    graph_ms = {"quantize+gemm": time_graph(split)}
     if use_fused:
-        capture(fused, "graph_fused")
-        graph_ms["fused"], _, _ = time_loop([lambda s: s["graph_fused"].replay()], False)
+        graph_ms["fused"] = time_graph(fused)
+
+    # Per-launch duration of one kernel: `steps` launches of it alone, back to
+    # back over the buffer sets, replayed from a graph (no host launch cost),
+    # with HIP events on the launch stream around the whole loop and none
+    # between launches: the kernel's duration plus the dispatch gap between
+    # two launches, without the gap each event marker adds (which dominates
+    # short kernels).
+    def time_alone(f):
+        return time_graph([f]) / steps
+
+    q_alone, g_alone = time_alone(split[0]), time_alone(split[1])
+    if use_fused:
+        fused_res["alone"] = time_alone(fused[0])
 
     # --- the transforms side by side on this workload's activations: the
     # quantizer alone (the GEMM does not depend on the transform)
@@ -338,11 +372,9 @@ def gpu_leg(name: str, steps: int, warmup: int):
     del src, dst
 
     props = torch.cuda.get_device_properties(dev)
-    for s in sets:
-        s.pop("graph_split", None)
-        s.pop("graph_fused", None)
     ceiling = mfma_ceiling(dev, stream, props.multi_processor_count)
-    return dict(ceiling=ceiling, m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms, graph_ms=graph_ms,
+    return dict(ceiling=ceiling, m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms,
+                q_alone=q_alone, g_alone=g_alone, graph_ms=graph_ms,
                 fused=fused_res, copy_gbps=copy_gbps, transforms=transforms, wfit=wfit, requant=requant_ms, nsets=nsets, device=props.name,
                 cus=props.multi_processor_count, arch=getattr(props, "gcnArchName", ""))
 
@@ -457,8 +489,15 @@ def main():
     per_path = {}
     for (p, lch), v in cands.items():
         per_path.setdefault(p, {})[lch] = round(v / args.steps, 5)
-    g_us = float(np.mean(g["g_ms"])) * 1e3
-    q_us = float(np.mean(g["q_ms"])) * 1e3
+    # per-launch durations: each kernel launched back to back on its own;
+    # the statistics of the loop with an event marker around every launch
+    # (each marker adds a dispatch gap) are reported beside them
+    g_us = g["g_alone"] * 1e3
+    q_us = g["q_alone"] * 1e3
+
+    def marked(ms):
+        return {"mean": round(float(np.mean(ms)) * 1e3, 2), "median": round(float(np.median(ms)) * 1e3, 2),
+                "min": round(float(np.min(ms)) * 1e3, 2)}
     g_tflops = flops / (g_us * 1e-6) / 1e12
     x_bytes = m * k * (2 if wl.x_dtype == "bf16" else 4)
     q_bytes = x_bytes + m * k // 2 + m * k // 32
@@ -477,22 +516,20 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_MXFP4_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_MXFP4_TFLOPS, 4), "kernel": "gemm_large"}
-    roof.update({"traffic": traffic, "us_per_launch": round(g_us, 2),
-                 "us_median": round(float(np.median(g["g_ms"])) * 1e3, 2),
-                 "us_min": round(float(np.min(g["g_ms"])) * 1e3, 2), "algorithmic_bytes": g_bytes,
-                 "algorithmic_flops": flops})
+    roof.update({"traffic": traffic, "us_per_launch": round(g_us, 2), "us_marked": marked(g["g_ms"]),
+                 "algorithmic_bytes": g_bytes, "algorithmic_flops": flops})
     split_info = {"ms_per_step": per_path["quantize+gemm"], "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2)}
     fz = g["fused"]
     if best_path != "fused":
         # the two-launch path is the step; the fused figures, if any, are reported beside it
         fused_only = None if fz is None else {"ms_per_step": per_path["fused"],
-                                              "us_per_launch": round(float(np.mean(fz["ms"])) * 1e3, 2)}
+                                              "us_per_launch": round(fz["alone"] * 1e3, 2)}
         fz = None
     else:
         fused_only = None
     if fz is not None:
         # the step is the fused layer: one launch reads bf16 X and the MXFP4 weights, writes Y
-        f_us = float(np.mean(fz["ms"])) * 1e3
+        f_us = fz["alone"] * 1e3
         f_bytes = x_bytes + n * (k // 2 + k // 32) + y_bytes
         f_gbps = f_bytes / (f_us * 1e-6) / 1e9
         f_traffic = recorded_traffic("linear_small", args.workload,
@@ -501,8 +538,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(f_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(f_gbps / PEAK_HBM_GBPS, 4), "frac_of_copy": round(f_gbps / g["copy_gbps"], 4),
                 "kernel": "linear_small", "traffic": f_traffic,
-                "us_per_launch": round(f_us, 2), "us_median": round(float(np.median(fz["ms"])) * 1e3, 2),
-                "us_min": round(float(np.min(fz["ms"])) * 1e3, 2),
+                "us_per_launch": round(f_us, 2), "us_marked": marked(fz["ms"]),
                 "algorithmic_bytes": f_bytes, "algorithmic_flops": flops}
     metric = METRIC if args.workload == "flux_up" else \
         f"MXFP4 GEMM TFLOPS @ M={m},K={k},N={n} (% peak); quantize GB/s (% HBM)"
@@ -528,9 +564,7 @@ def main():
         "quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
                      "frac_of_copy": round(q_gbps / g["copy_gbps"], 4),
-                     "traffic": q_traffic, "us_per_launch": round(q_us, 2),
-                     "us_median": round(float(np.median(g["q_ms"])) * 1e3, 2),
-                     "us_min": round(float(np.min(g["q_ms"])) * 1e3, 2),
+                     "traffic": q_traffic, "us_per_launch": round(q_us, 2), "us_marked": marked(g["q_ms"]),
                      "algorithmic_bytes": q_bytes},
         "split": split_info if fz is not None else None,
         "fused": fused_only,

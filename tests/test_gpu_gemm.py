@@ -170,7 +170,11 @@ def test_small_m_shapes(m, n, k):
     check_full(ac, as_, bc, bs, "small-m")
 
 
-SMALL_M_TILED = [(1, 300, 128), (33, 1000, 12288), (64, 256, 384), (50, 4097, 1024), (16, 14336, 4096)]
+# K = 10240 at M = 16 gives each wave one whole 8-step chunk (scale bytes by
+# dword loads) and one partial chunk (predicated loads); K = 8192 at M = 32
+# covers two weight groups on whole chunks
+SMALL_M_TILED = [(1, 300, 128), (33, 1000, 12288), (64, 256, 384), (50, 4097, 1024), (16, 14336, 4096),
+                 (16, 520, 10240), (32, 777, 8192)]
 
 
 @pytest.mark.parametrize("m,n,k", SMALL_M_TILED)
