@@ -68,7 +68,9 @@ template <bool BF16, int ROT, int P, int Q, bool FIT>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int dense) {
   constexpr int CPB = BF16 ? 4 : 8;   // 16-byte chunks per 32-element block
   __shared__ u32x4 slab[kThreads / 64][64 * CPB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: the per-wave address set-up (the division
+  // below, the layout branches) runs on the scalar unit
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t wid = blockIdx.x * (kThreads / 64) + wave;   // global wave index
   const uint32_t nblk = a.rows * a.nblk_row;
   const uint32_t nstage = a.nblk_row / 4;
@@ -101,17 +103,47 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
   const int esz = BF16 ? 2 : 4;
   const uint8_t* x = static_cast<const uint8_t*>(a.x);
 
-  // coalesced loads: instruction u covers chunks 64u .. 64u + 63 of the wave
+  // coalesced loads: instruction u covers chunks 64u .. 64u + 63 of the wave.
+  // A wave whose blocks all lie inside X (every wave but the last) loads
+  // without predicates; the edge wave loads zeros past the end.
+  const bool all_in = a.tiled ? rg * 16 + 16 <= a.rows : wb0 + 64 <= nblk;
   u32x4 ld[CPB];
+  if (all_in && a.tiled) {
+    // tiled order: the wave's input is rows 16 rg .. 16 rg + 15, elements
+    // 128 st .. 128 st + 127 of each, i.e. CPR 16-byte chunks per row; chunk
+    // c = 64 u + lane sits in row c / CPR at byte 16 (c % CPR)
+    constexpr int CPR = 4 * CPB;
+    const int64_t rstride = a.ld_x * esz;
+    const uint8_t* base = x + ((int64_t)(rg * 16) * a.ld_x + (int64_t)st * 128) * esz +
+                          (lane / CPR) * rstride + (lane % CPR) * 16;
 #pragma unroll
-  for (int u = 0; u < CPB; ++u) {
-    const int c = 64 * u + lane;
-    uint32_t row, col;
-    if (locate(c / CPB, row, col)) {
+    for (int u = 0; u < CPB; ++u)
+      ld[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + u * (64 / CPR) * rstride));
+  } else if (all_in && dense) {
+    // dense row-major rows: the wave's 64 blocks are one contiguous run
+    const uint8_t* base = x + (int64_t)wb0 * 32 * esz + lane * 16;
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) ld[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + u * 1024));
+  } else if (all_in) {
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int c = 64 * u + lane;
+      uint32_t row, col;
+      locate(c / CPB, row, col);
       const int64_t off = ((int64_t)row * a.ld_x + (int64_t)col * 32) * esz;
       ld[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off + 16 * (c % CPB)));
-    } else {
-      ld[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int c = 64 * u + lane;
+      uint32_t row, col;
+      if (locate(c / CPB, row, col)) {
+        const int64_t off = ((int64_t)row * a.ld_x + (int64_t)col * 32) * esz;
+        ld[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off + 16 * (c % CPB)));
+      } else {
+        ld[u] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
 #pragma unroll
