@@ -295,18 +295,9 @@ def gpu_leg(name: str, steps: int, warmup: int):
 
     # --- the transforms side by side on this workload's activations: the
     # quantizer alone (the GEMM does not depend on the transform)
-    def time_parts(fn, reps=50):
-        for i in range(5):
-            fn(sets[i % nsets])
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            fn(sets[i % nsets])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+    def time_parts(fn):
+        """ms per launch of one kernel, timed like time_alone."""
+        return time_alone(fn)
 
     trng = np.random.default_rng(1)
     tkinds = {"none": None, "h32": mx.HADAMARD32,
