@@ -452,7 +452,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
             for (int r = 0; r < 8; ++r) {
               const int row = 4 * r + (lane >> 4);
               const uint4 v = *reinterpret_cast<const uint4*>(tb + row * PITCH + (lane & 15) * 16);
-              *reinterpret_cast<uint4*>(static_cast<uint8_t*>(g.y) + ((int64_t)(m0 + row) * g.ld_y + n0) * ESZ) = v;
+              // non-temporal: Y streams out without displacing the operand
+              // panels the XCD's other workgroups still read from L2
+              __builtin_nontemporal_store(
+                  u32x4{v.x, v.y, v.z, v.w},
+                  reinterpret_cast<u32x4*>(static_cast<uint8_t*>(g.y) + ((int64_t)(m0 + row) * g.ld_y + n0) * ESZ));
             }
           }
         }
