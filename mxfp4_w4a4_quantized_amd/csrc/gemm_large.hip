@@ -101,6 +101,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+// One accumulator read straight from its AGPR.  The MXFP4-output epilogue
+// reads its accumulators through this, one fragment at a time; plain reads
+// let the register allocator copy all 256 out of the AGPRs at the loop exit,
+// which spilled.
+__device__ __forceinline__ float acc_read(float x) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+}
+
 __device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = GROUP_M * tiles_n;
   const int grp = L / per_group;
@@ -379,22 +389,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
         const bool row_ok = m < g.m;
 #pragma unroll
         for (int a = 0; a < FN; ++a) {
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = acc_read(acc[a][bb][r]);
           float am = 0.0f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(acc[a][bb][r]));
+          for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
           am = fmaxf(am, __shfl_xor(am, 32));
           const uint32_t ef = __float_as_uint(am) >> 23;
           const uint32_t sb = ef > 2u ? ef - 2u : 0u;
           const float sc = __uint_as_float(sb ? sb << 23 : 0x00400000u);
           uint32_t w0 = 0, w1 = 0;   // runs t = 0, 1 and t = 2, 3: two code bytes per run
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, acc[a][bb][0], acc[a][bb][1], sc, 0);
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, acc[a][bb][2], acc[a][bb][3], sc, 1);
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, acc[a][bb][4], acc[a][bb][5], sc, 2);
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, acc[a][bb][6], acc[a][bb][7], sc, 3);
-          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, acc[a][bb][8], acc[a][bb][9], sc, 0);
-          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, acc[a][bb][10], acc[a][bb][11], sc, 1);
-          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, acc[a][bb][12], acc[a][bb][13], sc, 2);
-          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, acc[a][bb][14], acc[a][bb][15], sc, 3);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[0], v[1], sc, 0);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[2], v[3], sc, 1);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[4], v[5], sc, 2);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[6], v[7], sc, 3);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[8], v[9], sc, 0);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[10], v[11], sc, 1);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[12], v[13], sc, 2);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[14], v[15], sc, 3);
           // group 0 keeps w0 (bytes 0-1, 4-5) and takes the partner's w0
           // (bytes 2-3, 6-7); group 1 keeps w1 (bytes 10-11, 14-15) and
           // takes the partner's w1 (bytes 8-9, 12-13)
