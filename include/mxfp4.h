@@ -89,7 +89,7 @@ extern "C" {
 typedef enum {
     MXFP4_OK = 0,
     MXFP4_ERR_INVALID_ARG = 1,  /* null pointer, bad size/stride, bad enum */
-    MXFP4_ERR_UNSUPPORTED = 2,  /* valid request this build does not run
+    MXFP4_ERR_UNSUPPORTED = 2,  /* valid request the library does not run
                                    (misaligned pointer, size beyond limits) */
     MXFP4_ERR_HIP = 3           /* a HIP runtime call or launch failed */
 } mxfp4_status;
