@@ -101,10 +101,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// One accumulator read straight from its AGPR.  The MXFP4-output epilogue
-// reads its accumulators through this, one fragment at a time; plain reads
-// let the register allocator copy all 256 out of the AGPRs at the loop exit,
-// which spilled.
+// One accumulator read straight from its AGPR.  The epilogues read their
+// accumulators through this, one fragment at a time: with plain reads the
+// register allocator copied all 256 out of the AGPRs at the loop exit in the
+// MXFP4-output epilogue (which spilled), and paired each read with its pack
+// through two temporaries in the bf16 one.
 __device__ __forceinline__ float acc_read(float x) {
   float r;
   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
@@ -445,19 +446,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
 #pragma unroll
           for (int a0 = 0; a0 < FN; a0 += FPP) {
 #pragma unroll
-            for (int a = a0; a < a0 + FPP; ++a)
+            for (int a = a0; a < a0 + FPP; ++a) {
+              // bf16: the fragment's 16 accumulators first, then the packs
+              // (plain reads went through two temporaries, one pair at a time)
+              float v[16];
+              if constexpr (BF16OUT) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[r] = acc_read(acc[a][bb][r]);
+              }
 #pragma unroll
               for (int t = 0; t < 4; ++t) {
                 uint8_t* dst = tb + lr * PITCH + ((a - a0) * 32 + 8 * t + 4 * lg) * ESZ;
                 if constexpr (BF16OUT) {
-                  *reinterpret_cast<uint2*>(dst) =
-                      make_uint2(pack_bf16(acc[a][bb][4 * t], acc[a][bb][4 * t + 1]),
-                                 pack_bf16(acc[a][bb][4 * t + 2], acc[a][bb][4 * t + 3]));
+                  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(v[4 * t], v[4 * t + 1]),
+                                                              pack_bf16(v[4 * t + 2], v[4 * t + 3]));
                 } else {
                   *reinterpret_cast<float4*>(dst) = make_float4(acc[a][bb][4 * t], acc[a][bb][4 * t + 1],
                                                                 acc[a][bb][4 * t + 2], acc[a][bb][4 * t + 3]);
                 }
               }
+            }
             // the area is private to this wave: its LDS writes land before its reads
             const int m0 = tm * BM + wm * (BM / WM) + 32 * bb;
             const int64_t n0 = tn * BN + wn * (BN / WN) + a0 * 32 + (lane & 15) * (16 / ESZ);
