@@ -88,12 +88,16 @@ __device__ __forceinline__ void kron32(const float* __restrict__ fa, const float
 // E8M0 byte of the block rule: floor(log2 amax) - 2 clamped at -127 is the
 // biased exponent field of amax minus 2 (subnormal and zero amax have field 0
 // and clamp).
+__device__ __forceinline__ uint32_t sbyte_of_amax(float amax) {
+  const uint32_t ef = __float_as_uint(amax) >> 23;
+  return ef > 2u ? ef - 2u : 0u;
+}
+
 __device__ __forceinline__ uint32_t rule_sbyte(const float (&v)[32]) {
   float amax = 0.0f;   // exact
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const uint32_t ef = __float_as_uint(amax) >> 23;
-  return ef > 2u ? ef - 2u : 0u;
+  return sbyte_of_amax(amax);
 }
 
 // The block scale 2^(sbyte - 127) as fp32 (2^-127 is the subnormal 0x00400000).

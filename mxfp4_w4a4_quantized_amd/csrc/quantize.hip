@@ -29,6 +29,9 @@
 // Every fp32 operation below is a single IEEE operation in a fixed order (the
 // library is compiled with -ffp-contract=off and the only fused operations
 // are explicit fmaf calls), so codes and scales are reproducible bit for bit.
+//
+// Small inputs with a Kronecker transform (at most 16384 blocks, p <= 16) use a
+// second kernel that spreads each block's transform over q lanes (below).
 #include "internal.h"
 #include "block_quant.h"
 
@@ -197,6 +200,121 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
   }
 }
 
+// Few blocks with a Kronecker transform (decode-sized inputs, which fill a
+// fraction of the chip): there the time is the latency of one lane's P*Q*(P+Q)
+// dependent-chain FMAs, so each block is spread over Q lanes instead of one.
+// Lane k of a block's group computes column k of the first stage, U[j][k] for
+// every j, and then the outputs y[Q*i+k] of the second stage -- the same
+// chains, in the same order, as the one-lane transform, so the values are
+// identical.  The group then takes the block amax with a butterfly of max
+// reductions, converts its P values at the block scale, merges the nibbles
+// with OR butterflies, and its first lane stores the 16 code bytes and the
+// scale byte.  Blocks are numbered row-major over the rows that the output
+// layout holds (tiled: whole 16-row groups, padding rows from zero inputs).
+template <bool BF16, int P, int Q>
+__global__ __launch_bounds__(kThreads) void quantize_kron_lanes_kernel(QuantArgs a, uint32_t nblocks) {
+  static_assert(P * Q == 32 && Q >= 2 && Q <= 32, "factor sizes");
+  const int lane = threadIdx.x & 63;
+  const int k = lane % Q;
+  const uint32_t blk = (blockIdx.x * kThreads + threadIdx.x) / Q;
+  const bool live = blk < nblocks;
+  const uint32_t row = live ? blk / a.nblk_row : 0u;
+  const uint32_t col = live ? blk - row * a.nblk_row : 0u;
+
+  float v[32];
+  if (live && row < a.rows) {
+    const uint8_t* src = static_cast<const uint8_t*>(a.x) + ((int64_t)row * a.ld_x + (int64_t)col * 32) * (BF16 ? 2 : 4);
+    if constexpr (BF16) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * c + 2 * j] = bf16_lo(q[j]);
+          v[8 * c + 2 * j + 1] = bf16_hi(q[j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * c + j] = __uint_as_float(q[j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+
+  // the block as the P x Q matrix Xm[j][l] = v[Q*j+l]; factors are uniform
+  const float* fa = a.fa;
+  const float* fb = a.fb;
+  float u[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    float acc = fb[k * Q] * v[Q * j];
+#pragma unroll
+    for (int l = 1; l < Q; ++l) acc = __builtin_fmaf(fb[k * Q + l], v[Q * j + l], acc);
+    u[j] = acc;
+  }
+  float y[P];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    float acc = fa[i * P] * u[0];
+#pragma unroll
+    for (int j = 1; j < P; ++j) acc = __builtin_fmaf(fa[i * P + j], u[j], acc);
+    y[i] = acc;
+    am = fmaxf(am, fabsf(acc));
+  }
+#pragma unroll
+  for (int o = 1; o < Q; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+  const uint32_t sbyte = sbyte_of_amax(am);
+  const float scale = scale_of(sbyte);
+
+  // element Q*i+k goes to nibble (Q*i+k) % 8 of code dword (Q*i+k) / 8
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int e = Q * i + k;
+    const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[i], 0.0f, scale, 0) & 0xFu;
+    const uint32_t sh = 4u * (uint32_t)(e & 7);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w[d] |= (e >> 3) == d ? c << sh : 0u;
+  }
+#pragma unroll
+  for (int o = 1; o < Q; o <<= 1) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w[d] |= (uint32_t)__shfl_xor((int)w[d], o);
+  }
+  if (!live || k != 0) return;
+  if (a.tiled) {
+    const uint32_t nstage = a.nblk_row / 4;
+    const uint32_t t = row / kTileRows, r = row % kTileRows, sg = col / 4, cb = col % 4;
+    const uint64_t ts = (uint64_t)t * nstage + sg;
+    uint4* dst = reinterpret_cast<uint4*>(a.codes + ts * (kTileRows * 64) + r * 64) + (cb ^ tiled_swz(r));
+    *dst = make_uint4(w[0], w[1], w[2], w[3]);
+    a.scales[ts * (kTileRows * 4) + r * 4 + cb] = static_cast<uint8_t>(sbyte);
+  } else {
+    const uint64_t gid = (uint64_t)row * a.nblk_row + col;
+    reinterpret_cast<uint4*>(a.codes)[gid] = make_uint4(w[0], w[1], w[2], w[3]);
+    a.scales[gid] = static_cast<uint8_t>(sbyte);
+  }
+}
+
+// Block counts up to this take the Q-lanes-per-block Kronecker kernel.
+#ifndef MXFP4_KRON_LANES_MAX_BLOCKS
+#define MXFP4_KRON_LANES_MAX_BLOCKS 16384
+#endif
+constexpr uint64_t kKronLanesMaxBlocks = MXFP4_KRON_LANES_MAX_BLOCKS;
+
+template <bool BF16, int P, int Q>
+void launch_kron_lanes(const QuantArgs& a, uint64_t blocks, hipStream_t s) {
+  const dim3 grid((uint32_t)((blocks * Q + kThreads - 1) / kThreads)), block(kThreads);
+  quantize_kron_lanes_kernel<BF16, P, Q><<<grid, block, 0, s>>>(a, (uint32_t)blocks);
+}
+
 template <bool BF16, bool FIT>
 hipError_t dispatch(const QuantArgs& a, hipStream_t s) {
   const uint64_t rows = a.tiled ? (a.rows + 15) / 16 * 16 : a.rows;   // tiled: whole 16-row groups
@@ -209,6 +327,15 @@ hipError_t dispatch(const QuantArgs& a, hipStream_t s) {
     quantize_kernel<BF16, 1, 1, 32, FIT><<<grid, block, 0, s>>>(a, dense);
   } else if (a.rot == 3) {
     quantize_kernel<BF16, 3, 1, 32, FIT><<<grid, block, 0, s>>>(a, dense);
+  } else if (!FIT && blocks <= kKronLanesMaxBlocks && a.p >= 1 && a.p <= 16) {
+    switch (a.p) {
+      case 1: launch_kron_lanes<BF16, 1, 32>(a, blocks, s); break;
+      case 2: launch_kron_lanes<BF16, 2, 16>(a, blocks, s); break;
+      case 4: launch_kron_lanes<BF16, 4, 8>(a, blocks, s); break;
+      case 8: launch_kron_lanes<BF16, 8, 4>(a, blocks, s); break;
+      case 16: launch_kron_lanes<BF16, 16, 2>(a, blocks, s); break;
+      default: return hipErrorInvalidValue;
+    }
   } else {
     switch (a.p) {
       case 1: quantize_kernel<BF16, 2, 1, 32, FIT><<<grid, block, 0, s>>>(a, dense); break;

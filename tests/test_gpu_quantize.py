@@ -72,11 +72,15 @@ def test_random_blocks(rows, k, rot, bf16):
     check(x, bf16, rot, f"random {rows}x{k}")
 
 
+# Up to 16384 blocks a Kronecker transform with p <= 16 runs on q lanes per
+# block, above that on one lane per block: 129 x 320 (1290 blocks) and
+# 700 x 1024 (22400 blocks) take one kernel each.
+@pytest.mark.parametrize("rows,k", [(129, 320), (700, 1024)], ids=["q-lanes", "one-lane"])
 @pytest.mark.parametrize("p,q", [(1, 32), (2, 16), (4, 8), (8, 4), (16, 2), (32, 1)])
 @pytest.mark.parametrize("bf16", [False, True])
-def test_kron_all_factorizations(p, q, bf16):
-    rng = np.random.default_rng(p * 100 + q)
-    x = workloads.random_blocks(rng, 129, 320)
+def test_kron_all_factorizations(p, q, bf16, rows, k):
+    rng = np.random.default_rng(p * 100 + q + rows)
+    x = workloads.random_blocks(rng, rows, k)
     if bf16:
         x = workloads.bf16_bits(x)
     check(x, bf16, rand_kron(p, q, p + 17 * q), f"kron {p}x{q}")
@@ -111,6 +115,9 @@ def test_edge_blocks_f32():
 
 def test_edge_blocks_kron():
     check(edge_blocks(1.0e36), False, rand_kron(4, 8, 3), "edge kron")
+    # 700 copies (36400 blocks): the one-lane kernel
+    check(np.tile(edge_blocks(1.0e36), (700, 1)), False, rand_kron(4, 8, 3), "edge kron, one lane")
+    check(edge_blocks(1.0e36), False, rand_kron(16, 2, 4), "edge kron 16x2")
 
 
 def test_edge_blocks_bf16():
@@ -145,7 +152,7 @@ def test_strided_input_rows():
 
 @pytest.mark.parametrize("rows,k,bf16,rot", [
     (1, 128, True, None), (255, 256, True, "h32"), (300, 384, False, None), (513, 512, True, "kron"),
-    (1024, 3072, True, "h32"), (16, 4096, True, "kron")])
+    (1024, 3072, True, "h32"), (16, 4096, True, "kron"), (2000, 1024, True, "kron")])
 def test_tiled_layout_matches_oracle(rows, k, bf16, rot):
     """Tiled output (the GEMM-native layout): untiled on the host it must equal
     the oracle's codes and scales bit for bit.  The padding rows of the last
