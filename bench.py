@@ -23,8 +23,8 @@ Prints one JSON line:
   roofline    the dominant kernel (the GEMM, or the fused layer for decode
               shapes, bytes = bf16 X + MXFP4 W + Y), its launch time the mean
               over K launches of that kernel alone, back to back over the
-              buffer sets and replayed from a HIP graph, with HIP events on
-              the launch stream around the loop.  `us_marked` gives the mean, median and min of a loop of
+              buffer sets and replayed from HIP graphs of at least 64
+              launches, with HIP events on the launch stream around the loop.  `us_marked` gives the mean, median and min of a loop of
               the K steps with events around every launch (each marker adds a
               dispatch gap, which inflates short kernels).  Large M: the
               MFMA-bound large-tile kernel, algorithmic FLOPs per launch / its
@@ -245,29 +245,32 @@ def gpu_leg(name: str, steps: int, warmup: int):
     # around the whole replay loop.  The captured work is the eager steps',
     # kernel for kernel.
     def capture(parts, count):
-        for s in sets[:count]:
+        """One graph of `count` steps of `parts`, cycling over the buffer sets."""
+        seq = [sets[i % nsets] for i in range(count)]
+        for s in seq[:nsets]:
             for f in parts:
                 f(s)
         torch.cuda.synchronize()
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr):
-            for s in sets[:count]:
+            for s in seq:
                 for f in parts:
                     f(s)
         torch.cuda.synchronize()
         return gr
 
-    def time_graph(parts):
-        cycle = capture(parts, nsets)
-        rest = steps % nsets
+    def time_graph(parts, per_replay=None):
+        per = per_replay or nsets
+        cycle = capture(parts, per)
+        rest = steps % per
         tail = capture(parts, rest) if rest else None
-        for _ in range(max(1, warmup // nsets)):
+        for _ in range(max(1, warmup // per)):
             cycle.replay()
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        for _ in range(steps // nsets):
+        for _ in range(steps // per):
             cycle.replay()
         if tail is not None:
             tail.replay()
@@ -281,13 +284,16 @@ def gpu_leg(name: str, steps: int, warmup: int):
         graph_ms["fused"] = time_graph(fused)
 
     # Per-launch duration of one kernel: `steps` launches of it alone, back to
-    # back over the buffer sets, replayed from a graph (no host launch cost),
-    # with HIP events on the launch stream around the whole loop and none
-    # between launches: the kernel's duration plus the dispatch gap between
-    # two launches, without the gap each event marker adds (which dominates
-    # short kernels).
+    # back over the buffer sets, replayed from graphs of at least 64 launches
+    # (so that the host's graph-launch cost stays hidden behind the GPU work
+    # even for a few-microsecond kernel), with HIP events on the launch stream
+    # around the whole loop and none between launches: the kernel's duration
+    # plus the dispatch gap between two launches, without the gap each event
+    # marker adds (which dominates short kernels).
+    alone_per_replay = nsets * -(-64 // nsets)
+
     def time_alone(f):
-        return time_graph([f]) / steps
+        return time_graph([f], alone_per_replay) / steps
 
     q_alone, g_alone = time_alone(split[0]), time_alone(split[1])
     if use_fused:
