@@ -179,6 +179,30 @@ def test_tiled_layout_matches_oracle(rows, k, bf16, rot):
     assert (pc[r16:] == 0xFF).all() and (ps[r16:] == 0xFF).all()
 
 
+# Strided activation rows (ld_x > k) with a Kronecker transform, on the
+# q-lanes kernel (40 rows, 320 blocks) and on the one-lane kernel (1800 rows,
+# 18000 blocks), in both layouts and input dtypes.
+@pytest.mark.parametrize("rows", [40, 1800], ids=["q-lanes", "one-lane"])
+@pytest.mark.parametrize("layout", [mx.ROWMAJOR, mx.TILED], ids=["rowmajor", "tiled"])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_kron_strided_rows(rows, layout, bf16):
+    k, ld = 1280, 1408
+    rng = np.random.default_rng(rows + ld)
+    full = workloads.random_blocks(rng, rows, ld)
+    if bf16:
+        full = workloads.bf16_bits(full)
+    x = dev_x(full, bf16)[:, :k]
+    r = rand_kron(8, 4, rows)
+    announce("quantize kron strided", rows, k, ld, "bf16" if bf16 else "f32", layout)
+    c, sc = mx.quantize_rotate(x, r, layout=layout)
+    torch.cuda.synchronize()
+    got = (c.cpu().numpy(), sc.cpu().numpy())
+    if layout == mx.TILED:
+        got = mx.untile_host(got[0], got[1], rows)
+    ref = oracle.quantize(np.ascontiguousarray(full[:, :k]), rot=oracle_rot(r), bf16=bf16)
+    assert_same(got, ref, "kron strided")
+
+
 def test_tiled_strided_input():
     rng = np.random.default_rng(6)
     full = workloads.bf16_bits(workloads.random_blocks(rng, 70, 640))
