@@ -18,6 +18,12 @@ Checks, the same bars as the fixed-shape tests:
     product of the dequantized row norms (the derivation is in the GEMM
     tests); bf16 output the round-to-nearest-even bf16 of the same kernel's
     fp32 output.
+
+Two more draws use the same bars: the fused small-M layer (quantization
+inside the GEMM; bf16 activations, M <= 64, Kronecker 2 <= p <= 16), and the
+GEMM with an MXFP4 output on operands whose block exponents lie in [-1, 1],
+where Y is exact in fp32 and the requantized bytes must equal the oracle
+quantizer's on the oracle's Y.
 """
 import numpy as np
 import pytest
@@ -115,3 +121,71 @@ def test_random_layer_case(i):
     assert err <= TOL, f"normalized error {err:.3e}"
     if out == torch.bfloat16:
         assert torch.equal(y.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+
+
+FUSED_CASES = 24
+FUSED_ROTS = ["none", "h32", "smooth", "kron"]
+
+
+@pytest.mark.parametrize("i", range(FUSED_CASES))
+def test_random_fused_small_m_case(i):
+    rng = np.random.default_rng(9000 + i)
+    m = int(rng.integers(1, 65))
+    n = int(rng.integers(1, 3000))
+    tiled = rng.random() < 0.5
+    k = 32 * int(rng.integers(1, 129))
+    if tiled:
+        k = 128 * max(1, k // 128)
+    rot = FUSED_ROTS[int(rng.integers(0, 4))]
+    pq = KRON_PQ[int(rng.integers(0, len(KRON_PQ)))]
+    out = torch.float32 if rng.random() < 0.5 else torch.bfloat16
+    layout = mx.TILED if tiled else mx.ROWMAJOR
+    print(f"[case] fused sweep {i}: m={m} n={n} k={k} tiled={tiled} rot={rot}"
+          f"{pq if rot == 'kron' else ''} out={out}", flush=True)
+    xh = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
+    dev_rot, ref_rot = make_rot(rot, pq, k, rng)
+    wc, ws = workloads.random_mxfp4(rng, n, k)
+    wd = [to_dev(t) for t in (mx.tile_host(wc, ws) if tiled else (wc, ws))]
+    xd = to_dev(xh.view(np.int16)).view(torch.bfloat16)
+    y32 = mx.linear_small(xd, *wd, dev_rot, torch.float32, layout=layout, n=n)
+    y = mx.linear_small(xd, *wd, dev_rot, out, layout=layout, n=n)
+    torch.cuda.synchronize()
+    xc, xs = oracle.quantize(xh, rot=ref_rot, bf16=True)
+    ref = oracle.gemm(xc, xs, wc, ws)
+    den = np.outer(row_norms(xc, xs), row_norms(wc, ws))
+    diff = np.abs(y32.cpu().numpy().astype(np.float64) - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(den > 0, diff / den, np.where(diff == 0, 0.0, np.inf))
+    err = float(rel.max()) if rel.size else 0.0
+    assert err <= TOL, f"normalized error {err:.3e}"
+    if out == torch.bfloat16:
+        assert torch.equal(y.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+
+
+REQUANT_CASES = 16
+
+
+@pytest.mark.parametrize("i", range(REQUANT_CASES))
+def test_random_requant_case(i):
+    rng = np.random.default_rng(11000 + i)
+    m = int(rng.integers(65, 1500))
+    layout = mx.TILED if rng.random() < 0.5 else mx.ROWMAJOR
+    out_layout = mx.TILED if rng.random() < 0.5 else mx.ROWMAJOR
+    n = 128 * int(rng.integers(1, 12)) if out_layout == mx.TILED else 32 * int(rng.integers(1, 48))
+    k = 128 * int(rng.integers(1, 33))
+    print(f"[case] requant sweep {i}: m={m} n={n} k={k} layout={layout} out_layout={out_layout}", flush=True)
+    ac, as_ = workloads.random_mxfp4(rng, m, k, -1, 1)
+    bc, bs = workloads.random_mxfp4(rng, n, k, -1, 1)
+    dev = [to_dev(t) for t in ((*mx.tile_host(ac, as_), *mx.tile_host(bc, bs)) if layout == mx.TILED
+                               else (ac, as_, bc, bs))]
+    ref = oracle.gemm(ac, as_, bc, bs)
+    y32 = ref.astype(np.float32)
+    assert np.array_equal(y32.astype(np.float64), ref)   # every partial sum is exact in fp32
+    want_c, want_s = oracle.quantize(y32)
+    qc, qs = mx.gemm_requant(*dev, layout=layout, out_layout=out_layout, m=m, n=n)
+    torch.cuda.synchronize()
+    gc, gs = qc.cpu().numpy(), qs.cpu().numpy()
+    if out_layout == mx.TILED:
+        gc, gs = mx.untile_host(gc, gs, m)
+    assert np.array_equal(gs, want_s), f"{np.count_nonzero(gs != want_s)} scale bytes differ"
+    assert np.array_equal(gc, want_c), f"{np.count_nonzero(gc != want_c)} code bytes differ"
