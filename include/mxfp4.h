@@ -185,10 +185,12 @@ MXFP4_API mxfp4_status mxfp4_quantize_fit(const void* x, int32_t x_dtype,
  *           the block's E2M1 dot product, accumulated in fp32, rounded to
  *           bf16 (nearest-even) for BF16 output.
  *   Code pointers 16-byte aligned; TILED scale pointers 4-byte aligned.
+ * Limits: with TILED operands and m > 64, each operand's tiled code bytes
+ *   (256 * ceil(rows / 256) * k / 2) must stay below 2^32.
  * Errors: INVALID_ARG for null pointers (when m, n > 0), k % 32 != 0 (k % 128
  *   for TILED), k <= 0, negative sizes, ld_y < n, bad dtype or layout;
- *   UNSUPPORTED for misaligned pointers or m, n, k >= 2^30; HIP if the launch
- *   fails. */
+ *   UNSUPPORTED for misaligned pointers, m, n, k >= 2^30, or TILED operands
+ *   past the code-byte limit above; HIP if the launch fails. */
 MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
                                   int64_t k, int32_t layout, void* y, int32_t y_dtype, int64_t ld_y,
@@ -198,11 +200,13 @@ MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
  * the epilogue, per 32-element block along N (the next layer's K), by the
  * quantizer's rule (E8M0 from the block amax, RNE-saturating E2M1 codes; no
  * rotation), so the next layer reads MXFP4 activations without a bf16 round
- * trip.  The codes and scales equal mxfp4_quantize_rotate applied to the fp32
- * Y of mxfp4_gemm bit for bit.  The pages' kernel "produces output without
- * conversion back to FP16 or BF16" ("AMD Quark delivers MXFP4 quantization for
- * FLUX.1-dev ...", "MXFP4 quantization for diffusion models"); this entry point
- * is that reading of it.
+ * trip.  The epilogue runs in the kernel that mxfp4_gemm takes for the same
+ * operands (the decode kernel for m <= 64, the large-tile kernel above), on
+ * the same fp32 sums: the codes and scales equal mxfp4_quantize_rotate
+ * applied to mxfp4_gemm's fp32 Y, bit for bit.  This is a reading of "AMD
+ * Quark delivers MXFP4 quantization for FLUX.1-dev ...", "MXFP4 quantization
+ * for diffusion models": the MXFP4 kernel hands on its result with no
+ * FP16/BF16 conversion in between.
  *   a_*, b_*, m, n, k, layout  as for mxfp4_gemm; k a multiple of 128.
  *   y_codes/y_scales  device (written): Y in `y_layout` -- ROWMAJOR
  *           [m][n/2] and [m][n/32], or TILED with m rows (padding rows not
@@ -210,7 +214,8 @@ MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
  * Errors: INVALID_ARG for null pointers (when m, n > 0), bad layouts, k <= 0
  *   or k % 32 (k % 128 for TILED operands), negative sizes; UNSUPPORTED for
  *   n % 32 != 0 (n % 128 for a TILED output), k % 128 != 0, misaligned
- *   pointers or sizes >= 2^30; HIP if the launch fails. */
+ *   pointers, sizes >= 2^30, or operands past the code-byte limit of
+ *   mxfp4_gemm (m > 64); HIP if the launch fails. */
 MXFP4_API mxfp4_status mxfp4_gemm_requant(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
                                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
                                           int64_t k, int32_t layout, uint8_t* y_codes, uint8_t* y_scales,
@@ -258,6 +263,19 @@ MXFP4_API mxfp4_status mxfp4_tiled_bytes(int64_t rows, int64_t k, int64_t* codes
  * Errors: INVALID_ARG for null pointers or n out of range, or a singular
  *   matrix (a zero pivot). */
 MXFP4_API mxfp4_status mxfp4_inverse_transpose(const float* m, int32_t n, float* out);
+
+/* Host helper for the offline weight fold of per-channel smoothing: the
+ * activations' column c is multiplied by r[c] (MXFP4_ROT_SMOOTH), so the
+ * weights' column c takes 1/r[c] and every product x[c] * w[c] is kept.
+ * The SmoothQuant-style scaling is the baseline "KroQuant: ..." compares its
+ * transform with (abstract); the inverse scaling goes on the weights.
+ *   r    host, k fp32 activation factors;  out  host, k fp32 (written):
+ *        out[c] = 1/r[c], the quotient formed in binary64 and rounded once to
+ *        fp32 (this equals the correctly rounded fp32 reciprocal).
+ * Errors: INVALID_ARG for null pointers, k <= 0, a factor that is zero or
+ *   not finite, or one whose reciprocal overflows fp32 (nothing is written
+ *   past the first such factor). */
+MXFP4_API mxfp4_status mxfp4_smooth_weight_factors(const float* r, int64_t k, float* out);
 
 /* Static description of a status code (never NULL). */
 MXFP4_API const char* mxfp4_status_string(int32_t status);

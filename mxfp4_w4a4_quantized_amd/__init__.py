@@ -47,7 +47,8 @@ HADAMARD32 = "h32"
 
 EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_quantize_fit", "mxfp4_gemm", "mxfp4_gemm_requant",
             "mxfp4_linear_small", "mxfp4_tiled_bytes",
-            "mxfp4_inverse_transpose", "mxfp4_status_string", "mxfp4_abi_version")
+            "mxfp4_inverse_transpose", "mxfp4_smooth_weight_factors", "mxfp4_status_string",
+            "mxfp4_abi_version")
 LINEAR_SMALL_MAX_M = 64
 
 
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.mxfp4_tiled_bytes.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.mxfp4_inverse_transpose.restype = i32
     L.mxfp4_inverse_transpose.argtypes = [vp, i32, vp]
+    L.mxfp4_smooth_weight_factors.restype = i32
+    L.mxfp4_smooth_weight_factors.argtypes = [vp, i64, vp]
     L.mxfp4_status_string.restype = ctypes.c_char_p
     L.mxfp4_status_string.argtypes = [i32]
     L.mxfp4_abi_version.restype = i32
@@ -142,13 +145,24 @@ class Smooth:
         return Smooth(torch.from_numpy(np.ascontiguousarray(r, np.float32).ravel()).to(device))
 
     def weight_side(self) -> "Smooth":
-        """Factors 1 / r[c] (binary64 reciprocal rounded to fp32), for folding
-        the inverse scaling into W."""
-        r = self.r.cpu().numpy().astype(np.float64)
-        return Smooth.from_host((1.0 / r).astype(np.float32), self.r.device)
+        """Factors 1 / r[c] from the library (binary64 quotient rounded to
+        fp32), for folding the inverse scaling into W."""
+        return Smooth.from_host(smooth_weight_factors(self.r.cpu().numpy()), self.r.device)
 
 
-def _rot_desc(rot, device):
+def _on_device(device, **tensors):
+    """Every tensor must live on one GPU, `device` (the first operand's):
+    the library takes device pointers and would fault on host memory."""
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device} (all operands on one GPU)")
+
+
+def _rot_desc(rot, device, k: int):
+    """Rotation descriptor for a call over k columns, with its factor tensors
+    (kept alive for the call) checked for shape, dtype and device."""
     if rot is None:
         return None, ()
     if isinstance(rot, str):
@@ -160,11 +174,17 @@ def _rot_desc(rot, device):
         for t in (a, b):
             if t.dtype != torch.float32 or not t.is_contiguous() or t.device != device:
                 raise ValueError("Kron factors must be contiguous fp32 tensors on the input's device")
-        return RotationDesc(ROT_KRON, a.shape[0], b.shape[0], 0, a.data_ptr(), b.data_ptr()), (a, b)
+        p, q = (a.shape[0] if a.dim() == 2 else 0), (b.shape[0] if b.dim() == 2 else 0)
+        if tuple(a.shape) != (p, p) or tuple(b.shape) != (q, q) or p * q != 32:
+            raise ValueError(f"Kron factors must be p x p and q x q with p * q = 32, got "
+                             f"{tuple(a.shape)} and {tuple(b.shape)}")
+        return RotationDesc(ROT_KRON, p, q, 0, a.data_ptr(), b.data_ptr()), (a, b)
     if isinstance(rot, Smooth):
         r = rot.r
         if r.dtype != torch.float32 or not r.is_contiguous() or r.device != device:
             raise ValueError("smoothing factors must be a contiguous fp32 tensor on the input's device")
+        if r.numel() != k:
+            raise ValueError(f"smoothing needs one factor per column: {r.numel()} factors for k = {k}")
         return RotationDesc(ROT_SMOOTH, 0, 0, 0, r.data_ptr(), None), (r,)
     raise TypeError(f"bad rotation {rot!r}")
 
@@ -204,6 +224,8 @@ def quantize_rotate(x: torch.Tensor, rot=None, codes: torch.Tensor = None, scale
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, k = x.shape
+    _on_device(x.device, codes=codes, scales=scales)
+    desc, _keep = _rot_desc(rot, x.device, k)
     cshape, sshape = _out_shapes(rows, k, layout)
     if codes is None:
         codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
@@ -211,9 +233,10 @@ def quantize_rotate(x: torch.Tensor, rot=None, codes: torch.Tensor = None, scale
         scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
     if not (codes.is_contiguous() and scales.is_contiguous()):
         raise ValueError("codes and scales must be contiguous")
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise ValueError("codes and scales must be uint8")
     if tuple(codes.shape) != cshape or tuple(scales.shape) != sshape:
         raise ValueError(f"codes/scales must be {cshape} / {sshape}")
-    desc, _keep = _rot_desc(rot, x.device)
     fn = lib().mxfp4_quantize_fit if fit else lib().mxfp4_quantize_rotate
     st = fn(x.data_ptr(), _dtype_code(x.dtype), rows, k, x.stride(0),
             ctypes.byref(desc) if desc is not None else None, layout,
@@ -228,6 +251,7 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b
     `layout`); fp32 accumulation, fp32 or bf16 output [m, n].  For TILED
     operands the real row counts come from y, or from m and n."""
     k = a_codes.shape[1] * 2
+    _on_device(a_codes.device, a_scales=a_scales, b_codes=b_codes, b_scales=b_scales, y=y)
     if y is not None:
         m, n = y.shape
     if m is None:
@@ -259,6 +283,8 @@ def gemm_requant(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.T
     n % 128 == 0 for a TILED output; k % 128 == 0).  Returns (codes, scales) of Y in `out_layout`, the same
     bytes as quantize_rotate(fp32 Y)."""
     k = a_codes.shape[1] * 2
+    _on_device(a_codes.device, a_scales=a_scales, b_codes=b_codes, b_scales=b_scales,
+               y_codes=y_codes, y_scales=y_scales)
     if m is None:
         m = a_codes.shape[0]
     if n is None:
@@ -267,6 +293,9 @@ def gemm_requant(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.T
         cshape, sshape = _out_shapes(rows, k, layout)
         if tuple(c.shape) != cshape or tuple(sc.shape) != sshape:
             raise ValueError(f"operand {name}: codes/scales must be {cshape} / {sshape}")
+    for t in (a_codes, a_scales, b_codes, b_scales):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("codes and scales must be contiguous uint8 tensors")
     cshape, sshape = _out_shapes(m, n, out_layout)
     if y_codes is None:
         y_codes = torch.empty(cshape, dtype=torch.uint8, device=a_codes.device)
@@ -274,6 +303,9 @@ def gemm_requant(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.T
         y_scales = torch.empty(sshape, dtype=torch.uint8, device=a_codes.device)
     if tuple(y_codes.shape) != cshape or tuple(y_scales.shape) != sshape:
         raise ValueError(f"output codes/scales must be {cshape} / {sshape}")
+    for t in (y_codes, y_scales):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("output codes and scales must be contiguous uint8 tensors")
     st = lib().mxfp4_gemm_requant(a_codes.data_ptr(), a_scales.data_ptr(), m, b_codes.data_ptr(),
                                   b_scales.data_ptr(), n, k, layout, y_codes.data_ptr(), y_scales.data_ptr(),
                                   out_layout, _stream(a_codes.device))
@@ -299,6 +331,8 @@ def linear_small(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     m, k = x.shape
+    _on_device(x.device, w_codes=w_codes, w_scales=w_scales, y=y)
+    desc, _keep = _rot_desc(rot, x.device, k)
     if n is None:
         n = w_codes.shape[0]
     cshape, sshape = _out_shapes(n, k, layout)
@@ -311,7 +345,6 @@ def linear_small(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
         y = torch.empty((m, n), dtype=out_dtype, device=x.device)
     if y.dim() != 2 or tuple(y.shape) != (m, n) or y.stride(1) != 1:
         raise ValueError("y must be [m, n] with unit column stride")
-    desc, _keep = _rot_desc(rot, x.device)
     st = lib().mxfp4_linear_small(
         x.data_ptr(), _dtype_code(x.dtype), m, k, x.stride(0),
         ctypes.byref(desc) if desc is not None else None,
@@ -366,6 +399,15 @@ def untile_host(tcodes: np.ndarray, tscales: np.ndarray, rows: int):
     c[ci] = np.ascontiguousarray(tcodes).reshape(-1)
     sc[si] = np.ascontiguousarray(tscales).reshape(-1)
     return c.reshape(rp, k // 2)[:rows], sc.reshape(rp, k // 32)[:rows]
+
+
+def smooth_weight_factors(r: np.ndarray) -> np.ndarray:
+    """fp32(1/r[c]) for activation smoothing factors r (library helper)."""
+    r = np.ascontiguousarray(r, dtype=np.float32).ravel()
+    out = np.empty(r.size, np.float32)
+    _check(lib().mxfp4_smooth_weight_factors(r.ctypes.data, r.size, out.ctypes.data),
+           "mxfp4_smooth_weight_factors")
+    return out
 
 
 def inverse_transpose(m: np.ndarray) -> np.ndarray:

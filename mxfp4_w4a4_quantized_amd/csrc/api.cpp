@@ -155,6 +155,9 @@ MXFP4_API mxfp4_status mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scale
   g.ld_y = ld_y;
   g.y_bf16 = (y_dtype == MXFP4_BF16);
   g.tiled = tiled;
+  // tiled operands with m > 64 run on the large-tile kernel only, whose
+  // operand offsets are 32-bit: code bytes of each operand below 4 GiB
+  if (tiled && !mxfp4::gemm_small_supported(g) && !mxfp4::gemm_large_supported(g)) return MXFP4_ERR_UNSUPPORTED;
   return from_hip(mxfp4::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
@@ -192,6 +195,9 @@ MXFP4_API mxfp4_status mxfp4_gemm_requant(const uint8_t* a_codes, const uint8_t*
   g.q_tiled = (y_layout == MXFP4_LAYOUT_TILED);
   g.q_codes = y_codes;
   g.q_scales = y_scales;
+  // the kernel that mxfp4_gemm takes for the same operands, so that the
+  // requantized Y is the one mxfp4_gemm returns in fp32
+  if (mxfp4::gemm_small_supported(g)) return from_hip(mxfp4::launch_gemm_small(g, static_cast<hipStream_t>(stream)));
   if (!mxfp4::gemm_large_supported(g)) return MXFP4_ERR_UNSUPPORTED;
   return from_hip(mxfp4::launch_gemm_large(g, static_cast<hipStream_t>(stream)));
 }
@@ -240,6 +246,20 @@ MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_
   L.g.y_bf16 = (y_dtype == MXFP4_BF16);
   L.g.tiled = tiled;
   return from_hip(mxfp4::launch_linear_small(L, static_cast<hipStream_t>(stream)));
+}
+
+// Reciprocals of the activation-side smoothing factors, for the weight fold:
+// the quotient 1/r is formed in binary64 and rounded once to fp32.
+MXFP4_API mxfp4_status mxfp4_smooth_weight_factors(const float* r, int64_t k, float* out) {
+  if (r == nullptr || out == nullptr || k <= 0) return MXFP4_ERR_INVALID_ARG;
+  for (int64_t c = 0; c < k; ++c) {
+    const float v = r[c];
+    if (!std::isfinite(v) || v == 0.0f) return MXFP4_ERR_INVALID_ARG;
+    const float w = static_cast<float>(1.0 / static_cast<double>(v));
+    if (!std::isfinite(w)) return MXFP4_ERR_INVALID_ARG;
+    out[c] = w;
+  }
+  return MXFP4_OK;
 }
 
 // Binary64 Gauss-Jordan elimination with partial pivoting on [M | I]; the

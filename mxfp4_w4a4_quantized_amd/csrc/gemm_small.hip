@@ -153,11 +153,59 @@ __device__ __forceinline__ void scales_dw(const Operand& o, int s0, int lane, in
   }
 }
 
-template <int MG, int NG, bool BF16OUT, bool TILED>
+// MXFP4 output of the small-M kernel: Y requantized per 32-block along N by
+// the quantizer's rule, from the same fp32 sums that the fp32 output stores.
+// The workgroup's 32 weight rows (NG = 2) are one block of each output row:
+// lane (r, g) holds columns 4g .. 4g + 3 of fragment 0 (v0) and of fragment 1
+// (v1), i.e. code bytes 2g, 2g + 1 and 8 + 2g, 8 + 2g + 1 of row r's block.
+// The block amax comes from the four lanes of row r (an exact max), the codes
+// from the E2M1 converter at the block scale, and lane (r, 0) gathers the 16
+// code bytes and stores them with the scale byte.
+__device__ __forceinline__ void store_requant(const GemmArgs& g, int m, int n0, const v4f& v0, const v4f& v1,
+                                              int lane) {
+  float am = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) am = fmaxf(am, fmaxf(fabsf(v0[r]), fabsf(v1[r])));
+  am = fmaxf(am, __shfl_xor(am, 16));
+  am = fmaxf(am, __shfl_xor(am, 32));
+  const uint32_t sbyte = blockq::sbyte_of_amax(am);
+  const float sc = blockq::scale_of(sbyte);
+  uint32_t w0 = 0, w1 = 0;
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v0[0], v0[1], sc, 0);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v0[2], v0[3], sc, 1);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v1[0], v1[1], sc, 0);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v1[2], v1[3], sc, 1);
+  const int lr = lane & 15;
+  uint32_t p0[4], p1[4];   // the low 16 bits of w0, w1 of lanes (r, 0..3)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    p0[j] = (uint32_t)__shfl((int)w0, lr + 16 * j) & 0xFFFFu;
+    p1[j] = (uint32_t)__shfl((int)w1, lr + 16 * j) & 0xFFFFu;
+  }
+  if ((lane >> 4) != 0 || m >= g.m) return;
+  const uint4 codes = make_uint4(p0[0] | (p0[1] << 16), p0[2] | (p0[3] << 16), p1[0] | (p1[1] << 16),
+                                 p1[2] | (p1[3] << 16));
+  const int blk = n0 >> 5;
+  if (g.q_tiled) {
+    const uint32_t r8 = (uint32_t)m & 255u, c = (uint32_t)blk & 3u;
+    const uint64_t ts = (uint64_t)((uint32_t)m >> 8) * ((uint32_t)g.n >> 7) + ((uint32_t)blk >> 2);
+    *reinterpret_cast<uint4*>(g.q_codes + ts * 16384 + r8 * 64 + 16 * (c ^ tiled_swz((int)r8))) = codes;
+    g.q_scales[ts * 1024 + r8 * 4 + c] = (uint8_t)sbyte;
+  } else {
+    *reinterpret_cast<uint4*>(g.q_codes + (int64_t)m * (g.n >> 1) + 16 * blk) = codes;
+    g.q_scales[(int64_t)m * (g.n >> 5) + blk] = (uint8_t)sbyte;
+  }
+}
+
+// OUT: 0 fp32 Y, 1 bf16 Y, 2 MXFP4 Y (NG == 2: one 32-block of each output
+// row per workgroup).
+template <int MG, int NG, int OUT, bool TILED>
 __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int spw, int y_vec) {
-  static_assert(MG * NG <= MAXACC, "reduction buffer holds MAXACC tiles per wave");
+  static_assert(MG * NG <= 2 * MAXACC, "reduction buffer size");
+  static_assert(OUT != 2 || NG == 2, "the MXFP4 output needs 32 weight rows per workgroup");
   static_assert(CH % 4 == 0, "dword scale loads cover 4 steps");
-  __shared__ v4f red[MAXW][MAXACC][64];
+  constexpr bool BF16OUT = OUT == 1;
+  __shared__ v4f red[MAXW][MG * NG][64];
 
   const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -261,6 +309,11 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
     }
   }
 
+  if constexpr (OUT == 2) {
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) store_requant(g, 16 * mg + lr, n0, acc[0][mg], acc[NG - 1][mg], lane);
+    return;
+  }
   // lane holds Y[16 mg + lr][n .. n + 3] of weight group q
 #pragma unroll
   for (int q = 0; q < NG; ++q)
@@ -292,20 +345,23 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
     }
 }
 
-template <int MG, int NG, bool BF16OUT, bool TILED>
+template <int MG, int NG, int OUT, bool TILED>
 void launch(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s) {
   const int grid = (g.n + 16 * NG - 1) / (16 * NG);
-  gemm_small_kernel<MG, NG, BF16OUT, TILED><<<grid, 64 * nwaves, 0, s>>>(g, spw, y_vec);
+  gemm_small_kernel<MG, NG, OUT, TILED><<<grid, 64 * nwaves, 0, s>>>(g, spw, y_vec);
 }
 
 template <int MG, int NG>
 void launch_mg(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s) {
-  if (g.y_bf16) {
-    if (g.tiled) launch<MG, NG, true, true>(g, nwaves, spw, y_vec, s);
-    else launch<MG, NG, true, false>(g, nwaves, spw, y_vec, s);
+  if (g.q_out) {
+    if (g.tiled) launch<MG, 2, 2, true>(g, nwaves, spw, y_vec, s);
+    else launch<MG, 2, 2, false>(g, nwaves, spw, y_vec, s);
+  } else if (g.y_bf16) {
+    if (g.tiled) launch<MG, NG, 1, true>(g, nwaves, spw, y_vec, s);
+    else launch<MG, NG, 1, false>(g, nwaves, spw, y_vec, s);
   } else {
-    if (g.tiled) launch<MG, NG, false, true>(g, nwaves, spw, y_vec, s);
-    else launch<MG, NG, false, false>(g, nwaves, spw, y_vec, s);
+    if (g.tiled) launch<MG, NG, 0, true>(g, nwaves, spw, y_vec, s);
+    else launch<MG, NG, 0, false>(g, nwaves, spw, y_vec, s);
   }
 }
 
@@ -513,7 +569,9 @@ hipError_t launch_fused_mg(const LinearArgs& L, int nwaves, int spw, int y_vec, 
 
 }  // namespace
 
-bool gemm_small_supported(const GemmArgs& g) { return g.m >= 1 && g.m <= 16 * MAXMG; }
+bool gemm_small_supported(const GemmArgs& g) {
+  return g.m >= 1 && g.m <= 16 * MAXMG && (!g.q_out || (g.n % (g.q_tiled ? 128 : 32)) == 0);
+}
 
 bool linear_small_supported(const LinearArgs& L) {
   return gemm_small_supported(L.g) && L.x_bf16 && (L.rot != 2 || (L.p >= 2 && L.p <= 16));

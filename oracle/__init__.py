@@ -24,7 +24,8 @@ What it computes (page titles and sections as the pages give them):
     for diffusion models" (no dequantization pass; output written as
     bf16/fp32).
   * per-channel smoothing (the SmoothQuant baseline the KroQuant page compares
-    against): one fp32 multiply per element by a per-channel factor.
+    against): one fp32 multiply per element by a per-channel factor; the
+    weight side multiplies by the correctly rounded reciprocal.
   * MXFP4 scale fitting -- "Bridging the Gap ...", "Methodologie: MR-GPTQ"
     item 2: the block exponent re-fitted among e0 - 1, e0, e0 + 1 by the
     smallest binary64 squared error (the rule is a reading; see the C source).
@@ -69,6 +70,7 @@ def _load():
         "oracle_fwht32": (None, [_f32p, _f32p]),
         "oracle_kron_apply": (None, [_f32p, _int, _f32p, _int, _f32p, _f32p]),
         "oracle_inverse_transpose": (_int, [_f32p, _int, _f32p]),
+        "oracle_smooth_weight_factors": (_int, [_f32p, _i64, _f32p]),
         "oracle_quantize_f32": (_int, [_f32p, _i64, _i64, _i64, _int, _f32p, _int, _f32p, _int, _u8p, _u8p]),
         "oracle_quantize_bf16": (_int, [_u16p, _i64, _i64, _i64, _int, _f32p, _int, _f32p, _int, _u8p, _u8p]),
         "oracle_quantize_f32_ex": (_int, [_f32p, _i64, _i64, _i64, _int, _f32p, _int, _f32p, _int, _int,
@@ -160,6 +162,16 @@ def inverse_transpose(m: np.ndarray) -> np.ndarray:
     out = np.empty((n, n), np.float32)
     if _load().oracle_inverse_transpose(m, n, out) != 0:
         raise ValueError("singular matrix")
+    return out
+
+
+def smooth_weight_factors(r: np.ndarray) -> np.ndarray:
+    """Weight side of per-channel smoothing: fp32(1/r[c]) for the activation
+    factors r (the quotient formed in binary64)."""
+    r = np.ascontiguousarray(r, dtype=np.float32).ravel()
+    out = np.empty(r.size, np.float32)
+    if _load().oracle_smooth_weight_factors(r, r.size, out) != 0:
+        raise ValueError("smoothing factors must be finite, nonzero, with finite fp32 reciprocals")
     return out
 
 

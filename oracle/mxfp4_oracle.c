@@ -219,6 +219,30 @@ int oracle_inverse_transpose(const float* m, int n, float* out)
     return 0;
 }
 
+/* Weight side of per-channel smoothing ([P4s]: the activations are divided
+ * by the smoothing factor s[c], the weights multiplied by it).  With the
+ * activation factor r[c] = 1/s[c] (the multiplier the quantizer applies),
+ * the weight factor is 1/r[c]: the quotient is formed in binary64 and
+ * rounded to fp32.  Binary64 has more than 2*24 + 2 bits, so this double
+ * rounding of a quotient of two fp32 values gives the correctly rounded fp32
+ * reciprocal.  Returns 0, or -1 if some r[c] is zero or not finite, or its
+ * reciprocal is not a finite fp32 (k < 0 is an error too). */
+int oracle_smooth_weight_factors(const float* r, int64_t k, float* out)
+{
+    int64_t c;
+    if (k < 0) return -1;
+    for (c = 0; c < k; ++c) {
+        double q;
+        float f;
+        if (!isfinite(r[c]) || r[c] == 0.0f) return -1;
+        q = 1.0 / (double)r[c];
+        f = (float)q;
+        if (!isfinite(f)) return -1;
+        out[c] = f;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Quantizer                                                                   */
 /* ------------------------------------------------------------------------- */

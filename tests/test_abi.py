@@ -11,6 +11,7 @@ import pytest
 
 import mxfp4_w4a4_quantized_amd as mx
 import oracle
+import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mxfp4.h")
@@ -214,15 +215,97 @@ def test_host_tiling_roundtrip_and_definition(rows, k):
 
 @pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32])
 def test_inverse_transpose_matches_oracle(n):
-    rng = np.random.default_rng(40 + n)
-    m = (np.eye(n) + 0.1 * rng.standard_normal((n, n))).astype(np.float32)
-    got = mx.inverse_transpose(m)
-    ref = oracle.inverse_transpose(m)
-    # both round a binary64 inverse to fp32: equal, or one ulp apart where the
-    # binary64 results straddle an fp32 rounding boundary
-    ulp = np.spacing(np.abs(ref))
-    assert np.all(np.abs(got - ref) <= ulp)
-    assert np.mean(got == ref) > 0.99
+    """The library's weight-side Kronecker factors are the oracle's, bit for
+    bit: both run Gauss-Jordan elimination with partial pivoting in binary64,
+    the same operations in the same order, and round once to fp32."""
+    for seed in range(40):
+        rng = np.random.default_rng(1000 * n + seed)
+        scale = 0.1 if seed % 2 == 0 else 1.0           # near-identity and general matrices
+        m = (np.eye(n) + scale * rng.standard_normal((n, n))).astype(np.float32)
+        got = mx.inverse_transpose(m)
+        ref = oracle.inverse_transpose(m)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"n={n} seed={seed}"
+
+
+def test_kron_workload_factors_match_oracle():
+    inp = workloads.make("llm_decode_kron", m=1)
+    for f in (inp["a"], inp["b"]):
+        assert np.array_equal(mx.inverse_transpose(f).view(np.uint32), oracle.inverse_transpose(f).view(np.uint32))
+
+
+def test_smooth_weight_factors_match_oracle():
+    rng = np.random.default_rng(7)
+    r = np.concatenate([(0.25 + 4 * rng.random(4096)),
+                        rng.random(4096) * np.exp2(rng.integers(-100, 100, 4096)) + 1e-30,
+                        np.exp2(np.arange(-126, 127))]).astype(np.float32)
+    r[::3] *= -1
+    got = mx.smooth_weight_factors(r)
+    assert np.array_equal(got.view(np.uint32), oracle.smooth_weight_factors(r).view(np.uint32))
+
+
+def test_smooth_weight_factors_errors():
+    L = mx.lib()
+    INV = mx.MXFP4_ERR_INVALID_ARG
+    out = np.empty(4, np.float32)
+    for bad in (0.0, np.inf, np.nan, 2.0 ** -149):
+        r = np.array([1.0, 2.0, bad, 4.0], np.float32)
+        assert L.mxfp4_smooth_weight_factors(r.ctypes.data, 4, out.ctypes.data) == INV
+    r = np.ones(4, np.float32)
+    assert L.mxfp4_smooth_weight_factors(None, 4, out.ctypes.data) == INV
+    assert L.mxfp4_smooth_weight_factors(r.ctypes.data, 0, out.ctypes.data) == INV
+    assert L.mxfp4_smooth_weight_factors(r.ctypes.data, 4, None) == INV
+    with pytest.raises(mx.Mxfp4Error):
+        mx.smooth_weight_factors(np.array([1.0, 0.0], np.float32))
+
+
+def test_gemm_tiled_code_byte_limit():
+    """TILED operands with m > 64 run on the kernel with 32-bit operand
+    offsets: past 4 GiB of tiled code bytes the call returns UNSUPPORTED
+    (synchronously, nothing launched)."""
+    A, T, UNS, OK = ALIGNED, mx.TILED, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
+    k = 8192                                       # 4 KiB of codes per row
+    big = (1 << 20)                                # 2^20 rows x 4 KiB = 4 GiB
+    assert g(A, A, big, A, A, 256, k, T, A, 0, 256, None) == UNS      # A too large
+    assert g(A, A, 256, A, A, big, k, T, A, 0, big, None) == UNS      # B too large
+    assert g(A, A, big - 256, A, A, 256, k, T, NULL, 0, 256, None) == mx.MXFP4_ERR_INVALID_ARG  # just below: null y
+    assert g(NULL, NULL, 0, NULL, NULL, big, k, T, NULL, 0, big, None) == OK   # m == 0: no-op
+
+
+def test_binding_rejects_host_tensors():
+    """The binding refuses tensors that are not on a GPU before any library
+    call: a host pointer handed to a kernel would fault the device."""
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    c = torch.zeros((4, 32), dtype=torch.uint8)
+    s = torch.zeros((4, 2), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        mx.quantize_rotate(x)
+    with pytest.raises(ValueError, match="GPU"):
+        mx.gemm(c, s, c, s)
+    with pytest.raises(ValueError, match="GPU"):
+        mx.gemm_requant(c, s, c, s)
+    with pytest.raises(ValueError, match="GPU"):
+        mx.linear_small(x, c, s)
+    with pytest.raises(ValueError, match="GPU"):
+        mx.linear(x, c, s)
+
+
+def test_binding_checks_rotation_factors():
+    """Kronecker factors must be p x p and q x q with p * q = 32; smoothing
+    needs exactly k factors (checked on meta tensors: no memory, no device)."""
+    import torch
+    dev = torch.device("meta")
+    f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    mx._rot_desc(mx.Kron(f(4, 4), f(8, 8)), dev, 64)
+    for a, b in ((f(4, 4), f(4, 4)), (f(4, 8), f(8, 8)), (f(16), f(2, 2)), (f(4, 4), f(8, 4))):
+        with pytest.raises(ValueError, match="Kron"):
+            mx._rot_desc(mx.Kron(a, b), dev, 64)
+    mx._rot_desc(mx.Smooth(f(64)), dev, 64)
+    for r in (f(32), f(65)):
+        with pytest.raises(ValueError, match="one factor per column"):
+            mx._rot_desc(mx.Smooth(r), dev, 64)
+    with pytest.raises(ValueError, match="input's device"):
+        mx._rot_desc(mx.Smooth(torch.zeros(64)), dev, 64)
 
 
 def test_inverse_transpose_errors():

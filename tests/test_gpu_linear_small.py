@@ -163,8 +163,9 @@ def test_fused_decode_workload():
     y_split = mx.linear(bf16_dev(inp["x"]), wc, ws, rot, torch.float32, layout=mx.TILED, n=wl.n)
     torch.cuda.synchronize()
     hwc, hws = mx.untile_host(wc.cpu().numpy(), ws.cpu().numpy(), wl.n)
-    wr = rot.weight_side()
-    rwc, rws = oracle.quantize(inp["w"], rot=("kron", wr.a.cpu().numpy(), wr.b.cpu().numpy()))
+    # weight side: the oracle's own inverse-transpose factors
+    rwc, rws = oracle.quantize(inp["w"], rot=("kron", oracle.inverse_transpose(inp["a"]),
+                                              oracle.inverse_transpose(inp["b"])))
     assert np.array_equal(hwc, rwc) and np.array_equal(hws, rws)
     xc, xs = oracle.quantize(inp["x"], rot=("kron", inp["a"], inp["b"]), bf16=True)
     ref = oracle.gemm(xc, xs, hwc, hws)

@@ -311,8 +311,9 @@ def test_fit_edge_blocks():
 
 def test_smoothed_linear_matches_oracle():
     """A smoothed linear layer: activations multiplied by r per channel, the
-    weights by 1/r (binary64 reciprocal rounded to fp32); the GEMM of the two
-    quantized operands against the oracle's."""
+    weights by 1/r (binary64 quotient rounded to fp32, the library's helper on
+    the device side and the oracle's on the reference side); the GEMM of the
+    two quantized operands against the oracle's."""
     rng = np.random.default_rng(40)
     m, n, k = 300, 260, 512
     x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
@@ -323,7 +324,8 @@ def test_smoothed_linear_matches_oracle():
     y = mx.linear(dev_x(x, True), wc, ws, sm, torch.float32)
     torch.cuda.synchronize()
     xc, xs = oracle.quantize(x, rot=oracle_rot_any(sm), bf16=True)
-    rwc, rws = oracle.quantize(w, rot=oracle_rot_any(sm.weight_side()))
+    # weight side: the oracle's own reciprocal factors
+    rwc, rws = oracle.quantize(w, rot=("smooth", oracle.smooth_weight_factors(sm.r.cpu().numpy())))
     assert np.array_equal(wc.cpu().numpy(), rwc) and np.array_equal(ws.cpu().numpy(), rws)
     ref = oracle.gemm(xc, xs, rwc, rws)
     den = np.outer(np.sqrt((oracle.dequantize(xc, xs) ** 2).sum(1)), np.sqrt((oracle.dequantize(rwc, rws) ** 2).sum(1)))

@@ -5,9 +5,10 @@ every partial sum of the GEMM a multiple of 2^-4 below 2^24 units, so Y is
 exact in fp32 whatever the summation order.  Then the oracle's Y (binary64,
 exact) is the kernel's Y, and the requantized output must equal the oracle's
 quantizer applied to it, code for code and scale for scale.  Realistic
-operands (wide exponents): invariants of the requantization against the same
-kernel's fp32 output -- the scale byte is the E8M0 rule of the block amax and
-every element is within the grid's rounding bound.
+operands (wide exponents, Y rounded in fp32): the requantized output must
+equal the oracle's quantizer applied to the fp32 Y that mxfp4_gemm returns for
+the same operands -- the epilogue requantizes the same sums in the same
+kernel.
 """
 import numpy as np
 import pytest
@@ -95,26 +96,56 @@ def test_requant_tiled_padding_untouched():
     assert (pc[m:] == 0xFF).all() and (ps[m:] == 0xFF).all()
 
 
-def test_requant_realistic_invariants():
-    rng = np.random.default_rng(6)
-    m, n, k = 520, 768, 1024
-    _, _, dac, das = operands(rng, m, k, -20, 20, T)
-    _, _, dbc, dbs = operands(rng, n, k, -20, 20, T)
-    announce("gemm_requant realistic", m, n, k)
-    qc, qs = mx.gemm_requant(dac, das, dbc, dbs, layout=T, m=m, n=n)
-    y = mx.gemm(dac, das, dbc, dbs, torch.float32, layout=T, m=m, n=n)
+REALISTIC = [(520, 768, 1024, T, T), (520, 768, 1024, R, R), (300, 512, 3072, T, R),
+             (16, 1024, 4096, T, T), (16, 1024, 4096, R, R), (64, 640, 1024, T, R), (5, 256, 512, R, T),
+             (40, 384, 2048, T, T)]
+
+
+@pytest.mark.parametrize("m,n,k,layout,out_layout", REALISTIC)
+def test_requant_realistic_bit_exact(m, n, k, layout, out_layout):
+    """Wide block exponents, so Y is rounded in fp32 and its summation order
+    matters: the requantized bytes must equal the oracle's quantizer applied
+    to the fp32 Y that mxfp4_gemm returns for the same operands (the decode
+    kernel for m <= 64, the large-tile kernel above), bit for bit."""
+    rng = np.random.default_rng(6 + m + n + k)
+    _, _, dac, das = operands(rng, m, k, -20, 20, layout)
+    _, _, dbc, dbs = operands(rng, n, k, -20, 20, layout)
+    announce("gemm_requant realistic", m, n, k, layout, out_layout)
+    qc, qs = mx.gemm_requant(dac, das, dbc, dbs, layout=layout, out_layout=out_layout, m=m, n=n)
+    y = mx.gemm(dac, das, dbc, dbs, torch.float32, layout=layout, m=m, n=n)
     torch.cuda.synchronize()
     y = y.cpu().numpy()
-    qc, qs = qc.cpu().numpy(), qs.cpu().numpy()
-    amax = np.abs(y).reshape(m, n // 32, 32).max(axis=2)
-    field = (amax.view(np.uint32) >> 23).astype(np.int64)          # biased exponent of the block amax
-    assert np.array_equal(qs.astype(np.int64), np.maximum(field - 2, 0))
-    lut = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
-    nib = np.stack([qc & 15, qc >> 4], axis=-1).reshape(m, n)
-    e = np.exp2(qs.astype(np.float64) - 127).repeat(32, axis=1)
-    yh = lut[nib] * e
-    assert (np.abs(yh - y) <= 2 * e).all()                          # RNE on the grid, saturation at 6
-    assert ((yh == 0) | (np.sign(yh) == np.sign(y))).all()          # signs kept
+    got = (qc.cpu().numpy(), qs.cpu().numpy())
+    if out_layout == T:
+        got = mx.untile_host(got[0], got[1], m)
+    want = oracle.quantize(y)
+    assert np.array_equal(got[1], want[1]), f"{np.count_nonzero(got[1] != want[1])} scale bytes differ"
+    assert np.array_equal(got[0], want[0]), f"{np.count_nonzero(got[0] != want[0])} code bytes differ"
+    # the case is not trivially exact: Y has rounded elements (inexact in any order)
+    ac, as_ = (mx.untile_host(dac.cpu().numpy(), das.cpu().numpy(), m) if layout == T
+               else (dac.cpu().numpy(), das.cpu().numpy()))
+    bc, bs = (mx.untile_host(dbc.cpu().numpy(), dbs.cpu().numpy(), n) if layout == T
+              else (dbc.cpu().numpy(), dbs.cpu().numpy()))
+    assert np.count_nonzero(y.astype(np.float64) != oracle.gemm(ac, as_, bc, bs)) > 0
+
+
+def test_requant_full_workload():
+    """The flux_up GEMM (3584 x 3072 -> 12288) in the benchmark's tiled
+    configuration with an MXFP4 output: bytes equal the oracle's quantizer on
+    the same kernel's fp32 Y."""
+    inp = workloads.make("flux_up")
+    wl = inp["wl"]
+    m, n, k = wl.m, wl.n, wl.k
+    x = to_dev(inp["x"].view(np.int16)).view(torch.bfloat16)
+    announce("gemm_requant flux_up", m, n, k)
+    wc, ws = mx.quantize_weight(to_dev(inp["w"]), None, layout=T)
+    xc, xs = mx.quantize_rotate(x, None, layout=T)
+    qc, qs = mx.gemm_requant(xc, xs, wc, ws, layout=T, out_layout=T, m=m, n=n)
+    y = mx.gemm(xc, xs, wc, ws, torch.float32, layout=T, m=m, n=n)
+    torch.cuda.synchronize()
+    got = mx.untile_host(qc.cpu().numpy(), qs.cpu().numpy(), m)
+    want = oracle.quantize(y.cpu().numpy())
+    assert np.array_equal(got[1], want[1]) and np.array_equal(got[0], want[0])
 
 
 def test_requant_rejects_unsupported():

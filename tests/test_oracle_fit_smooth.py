@@ -192,3 +192,68 @@ def test_smooth_is_one_fp32_multiply(bf16):
     assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
     # the rotation-only entry point applies the same multiply
     assert np.array_equal(oracle.rotate(xf, ("smooth", r)), np.multiply(xf, r[None, :], dtype=np.float32))
+
+
+# ------------------------------------------------ smoothing, weight side ---
+# The weight side of smoothing multiplies W by the reciprocal of the
+# activation factor ("KroQuant: ...", the SmoothQuant comparison: the scaling
+# the activations lose is folded into the weights).  The oracle forms it in
+# binary64 and rounds to fp32; pinned here against the exact rational
+# reciprocal, correctly rounded (ties to even), computed with fractions.
+
+def correctly_rounded_reciprocal(r: float) -> float:
+    q = 1 / Fraction(r)
+    f = np.float32(float(q))          # within one fp32 step of the exact value
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    dist = [abs(Fraction(float(c)) - q) for c in cands]
+    best = min(dist)
+    ties = [c for c, d in zip(cands, dist) if d == best]
+    if len(ties) > 1:                 # midpoint: the even significand wins
+        ties = [c for c in ties if (int(np.float32(c).view(np.uint32)) & 1) == 0]
+    return np.float32(ties[0])
+
+
+def test_smooth_weight_factors_are_correctly_rounded_reciprocals():
+    rng = np.random.default_rng(21)
+    mant = rng.random(3000) + 1.0
+    ex = rng.integers(-120, 121, 3000)
+    r = (mant * np.exp2(ex) * rng.choice([-1.0, 1.0], 3000)).astype(np.float32)
+    got = oracle.smooth_weight_factors(r)
+    want = np.array([correctly_rounded_reciprocal(float(v)) for v in r], np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_smooth_weight_factors_worked_values():
+    r = np.array([3.0, 0.1, 7.0, -0.75, 1.0], np.float32)
+    got = oracle.smooth_weight_factors(r).view(np.uint32)
+    # 1/3 rounds up to 0x3EAAAAAB; 1/0.1f is 9.99999985..., nearest fp32 is 10;
+    # 1/7 = 0x3E124925; -1/0.75 = -4/3 = 0xBFAAAAAB; 1/1 = 1
+    assert got.tolist() == [0x3EAAAAAB, 0x41200000, 0x3E124925, 0xBFAAAAAB, 0x3F800000]
+
+
+def test_smooth_weight_factors_powers_of_two_exact():
+    j = np.arange(-127, 128)
+    r = np.exp2(j).astype(np.float32)
+    got = oracle.smooth_weight_factors(r)
+    assert np.array_equal(got, np.exp2(-j).astype(np.float32))
+
+
+@pytest.mark.parametrize("bad", [0.0, -0.0, np.inf, -np.inf, np.nan, 2.0 ** -149])
+def test_smooth_weight_factors_reject_unusable_factors(bad):
+    with pytest.raises(ValueError):
+        oracle.smooth_weight_factors(np.array([1.0, bad], np.float32))
+
+
+def test_smooth_fold_preserves_block_products():
+    """Unquantized, (x * r) . (w / r) = x . w to binary32 rounding."""
+    rng = np.random.default_rng(22)
+    k = 256
+    x = rng.standard_normal((4, k)).astype(np.float32)
+    w = rng.standard_normal((5, k)).astype(np.float32)
+    r = (0.25 + 4 * rng.random(k)).astype(np.float32)
+    wr = oracle.smooth_weight_factors(r)
+    xs = oracle.rotate(x, ("smooth", r)).astype(np.float64)
+    ws = np.multiply(w, wr[None, :], dtype=np.float32).astype(np.float64)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    bound = 4 * 2.0 ** -24 * (np.abs(x).astype(np.float64) @ np.abs(w).astype(np.float64).T)
+    assert np.all(np.abs(xs @ ws.T - ref) <= bound)
