@@ -222,13 +222,14 @@ MXFP4_API mxfp4_status mxfp4_gemm_requant(const uint8_t* a_codes, const uint8_t*
                                           int32_t y_layout, void* stream);
 
 /* Fused small-M linear layer Y = Q(rot(X)) * W^T for decode shapes: the
- * activations are rotated and quantized inside the GEMM, each block straight
- * into the matrix-core operand registers, so the quantized activations never
- * reach memory and the layer is one launch.  The rotation "fused into the
- * quantization and matmul kernels" is the design of "Bridging the Gap Between
- * Promise and Performance for Microscaling FP4 Quantization", "GPU Kernel
- * Ondersteuning (QuTLASS)"; the quantization rule is the one above, so Y
- * equals mxfp4_quantize_rotate followed by mxfp4_gemm.
+ * activations are rotated and quantized inside the GEMM kernel, straight into
+ * the matrix-core operands, so the quantized activations never reach memory
+ * and the layer is one launch.  The rotation "fused into the quantization and
+ * matmul kernels" is the design of "Bridging the Gap Between Promise and
+ * Performance for Microscaling FP4 Quantization", "GPU Kernel Ondersteuning
+ * (QuTLASS)".  The quantized activations equal mxfp4_quantize_rotate's bit
+ * for bit; Y agrees with mxfp4_quantize_rotate followed by mxfp4_gemm within
+ * the GEMM's fp32 rounding (the K sums are taken in another order).
  *   x       device, [m][ld_x] BF16 activations, 16-byte aligned, ld_x a
  *           multiple of 8, ld_x >= k.
  *   rot     NULL / NONE, HADAMARD32, SMOOTH, or KRON with 2 <= p <= 16.
@@ -236,15 +237,35 @@ MXFP4_API mxfp4_status mxfp4_gemm_requant(const uint8_t* a_codes, const uint8_t*
  *   m       1 <= m <= 64 (0 is a no-op); n >= 0; k > 0 multiple of 32 (of
  *           128 for TILED).
  *   y       device, [m][ld_y] of y_dtype (F32 or BF16), ld_y >= n.
- * Errors: INVALID_ARG as for mxfp4_quantize_rotate and mxfp4_gemm;
- *   UNSUPPORTED for m > 64, F32 activations, a KRON rotation with p = 1 or
- *   p = 32, or misaligned pointers (use mxfp4_quantize_rotate + mxfp4_gemm
- *   there); HIP if the launch fails. */
+ *   workspace, workspace_bytes  device scratch for the split over K, of at
+ *           least mxfp4_linear_small_workspace(m, n, k) bytes, 256-byte
+ *           aligned (NULL and 0 when that size is 0, i.e. k <= 1024).  Its
+ *           first 64 KiB are counters of the groups of 256 weight rows, the
+ *           same region for every shape; they must be zero before the
+ *           workspace's first use (e.g. one hipMemset), and every call leaves
+ *           them zero when its kernel completes, so one workspace serves
+ *           calls of any shape in stream order.  Calls that may run at the
+ *           same time (other streams, other host threads) need workspaces of
+ *           their own.
+ * Errors: INVALID_ARG as for mxfp4_quantize_rotate and mxfp4_gemm, and for a
+ *   missing or short workspace; UNSUPPORTED for m > 64, F32 activations, a
+ *   KRON rotation with p = 1 or p = 32, or misaligned pointers (use
+ *   mxfp4_quantize_rotate + mxfp4_gemm there); HIP if the launch fails. */
 MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_t m, int64_t k,
                                           int64_t ld_x, const mxfp4_rotation* rot,
                                           const uint8_t* w_codes, const uint8_t* w_scales, int64_t n,
                                           int32_t layout, void* y, int32_t y_dtype, int64_t ld_y,
-                                          void* stream);
+                                          void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace size of mxfp4_linear_small for (m, n, k): 0 when k <= 1024 (one
+ * K slice), else 64 KiB of group counters plus ceil(k / 1024) fp32 partial
+ * tiles of m x 256 ceil(n / 256).  The fused layer over 16 x 4096 -> 14336
+ * needs 3.74 MB.
+ * Errors: INVALID_ARG for a null pointer, negative sizes, k not a positive
+ *   multiple of 32; UNSUPPORTED for m > 64, k >= 2^30, and, when k > 1024,
+ *   n > 4194304 (16384 counters) or partial tiles of 2 GiB or more
+ *   (mxfp4_linear_small returns UNSUPPORTED for the same shapes). */
+MXFP4_API mxfp4_status mxfp4_linear_small_workspace(int64_t m, int64_t n, int64_t k, int64_t* bytes);
 
 /* Buffer sizes of a TILED operand with `rows` rows and `k` columns (k > 0, a
  * multiple of 128; rows >= 0): *codes_bytes = 256 T * k / 2 and
@@ -281,7 +302,7 @@ MXFP4_API mxfp4_status mxfp4_smooth_weight_factors(const float* r, int64_t k, fl
 MXFP4_API const char* mxfp4_status_string(int32_t status);
 
 /* ABI version of this header (bumped on incompatible changes). */
-#define MXFP4_ABI_VERSION 2
+#define MXFP4_ABI_VERSION 3
 MXFP4_API int32_t mxfp4_abi_version(void);
 
 #ifdef __cplusplus

@@ -46,7 +46,7 @@ TILE_ROWS, TILE_K = 256, 128
 HADAMARD32 = "h32"
 
 EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_quantize_fit", "mxfp4_gemm", "mxfp4_gemm_requant",
-            "mxfp4_linear_small", "mxfp4_tiled_bytes",
+            "mxfp4_linear_small", "mxfp4_linear_small_workspace", "mxfp4_tiled_bytes",
             "mxfp4_inverse_transpose", "mxfp4_smooth_weight_factors", "mxfp4_status_string",
             "mxfp4_abi_version")
 LINEAR_SMALL_MAX_M = 64
@@ -86,7 +86,9 @@ def lib() -> ctypes.CDLL:
     L.mxfp4_gemm_requant.argtypes = [vp, vp, i64, vp, vp, i64, i64, i32, vp, vp, i32, vp]
     L.mxfp4_linear_small.restype = i32
     L.mxfp4_linear_small.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), vp, vp, i64, i32,
-                                     vp, i32, i64, vp]
+                                     vp, i32, i64, vp, i64, vp]
+    L.mxfp4_linear_small_workspace.restype = i32
+    L.mxfp4_linear_small_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
     L.mxfp4_tiled_bytes.restype = i32
     L.mxfp4_tiled_bytes.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.mxfp4_inverse_transpose.restype = i32
@@ -322,16 +324,41 @@ def linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, rot=N
     return gemm(a_codes, a_scales, w_codes, w_scales, out_dtype, y, layout=layout, m=x.shape[0], n=n)
 
 
+def linear_small_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Device workspace that mxfp4_linear_small needs for (m, n, k) (0 when K
+    fits one slice of 1024)."""
+    b = ctypes.c_int64()
+    _check(lib().mxfp4_linear_small_workspace(m, n, k, ctypes.byref(b)), "mxfp4_linear_small_workspace")
+    return b.value
+
+
+_workspaces = {}
+
+
+def _cached_workspace(device, stream: int, nbytes: int) -> torch.Tensor:
+    """A zero-filled workspace per (device, stream), grown on demand.  The
+    library leaves its counters at zero after every call, so one workspace
+    serves every call on its stream; calls on other streams get their own."""
+    key = (device.index, stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
 def linear_small(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, rot=None,
                  out_dtype=torch.bfloat16, y: torch.Tensor = None, layout: int = ROWMAJOR,
-                 n: int = None) -> torch.Tensor:
+                 n: int = None, workspace: torch.Tensor = None) -> torch.Tensor:
     """Fused small-M linear layer (decode): bf16 x [m, k] with 1 <= m <= 64 is
     rotated and quantized inside the GEMM (one launch, no quantized
-    activations in memory); same result as linear()."""
+    activations in memory); same result as linear() within the GEMM's fp32
+    rounding.  `workspace` (uint8, zero-filled before its first use) defaults
+    to one kept per device and stream."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     m, k = x.shape
-    _on_device(x.device, w_codes=w_codes, w_scales=w_scales, y=y)
+    _on_device(x.device, w_codes=w_codes, w_scales=w_scales, y=y, workspace=workspace)
     desc, _keep = _rot_desc(rot, x.device, k)
     if n is None:
         n = w_codes.shape[0]
@@ -345,11 +372,19 @@ def linear_small(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
         y = torch.empty((m, n), dtype=out_dtype, device=x.device)
     if y.dim() != 2 or tuple(y.shape) != (m, n) or y.stride(1) != 1:
         raise ValueError("y must be [m, n] with unit column stride")
+    stream = _stream(x.device)
+    need = linear_small_workspace_bytes(m, n, k) if m <= LINEAR_SMALL_MAX_M else 0
+    if workspace is None and need > 0:
+        workspace = _cached_workspace(x.device, stream, need)
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
     st = lib().mxfp4_linear_small(
         x.data_ptr(), _dtype_code(x.dtype), m, k, x.stride(0),
         ctypes.byref(desc) if desc is not None else None,
         w_codes.data_ptr(), w_scales.data_ptr(), n, layout,
-        y.data_ptr(), _dtype_code(y.dtype), y.stride(0), _stream(x.device))
+        y.data_ptr(), _dtype_code(y.dtype), y.stride(0),
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, stream)
     _check(st, "mxfp4_linear_small")
     return y
 

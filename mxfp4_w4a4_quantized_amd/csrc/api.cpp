@@ -202,10 +202,22 @@ MXFP4_API mxfp4_status mxfp4_gemm_requant(const uint8_t* a_codes, const uint8_t*
   return from_hip(mxfp4::launch_gemm_large(g, static_cast<hipStream_t>(stream)));
 }
 
+MXFP4_API mxfp4_status mxfp4_linear_small_workspace(int64_t m, int64_t n, int64_t k, int64_t* bytes) {
+  if (bytes == nullptr || m < 0 || n < 0 || k <= 0 || (k % 32) != 0) return MXFP4_ERR_INVALID_ARG;
+  if (m > 64) return MXFP4_ERR_UNSUPPORTED;
+  if (n >= kMaxDim || k >= kMaxDim) return MXFP4_ERR_UNSUPPORTED;
+  const int64_t need = (m == 0 || n == 0) ? 0 : mxfp4::linear_small_workspace_bytes(m, n, k);
+  if (need > 0 && (n > mxfp4::kLinearMaxN || need - mxfp4::kLinearCounterBytes >= (int64_t(1) << 31)))
+    return MXFP4_ERR_UNSUPPORTED;
+  *bytes = need;
+  return MXFP4_OK;
+}
+
 MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t ld_x,
                                           const mxfp4_rotation* rot, const uint8_t* w_codes,
                                           const uint8_t* w_scales, int64_t n, int32_t layout, void* y,
-                                          int32_t y_dtype, int64_t ld_y, void* stream) {
+                                          int32_t y_dtype, int64_t ld_y, void* workspace,
+                                          int64_t workspace_bytes, void* stream) {
   if (x_dtype != MXFP4_F32 && x_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
   if (y_dtype != MXFP4_F32 && y_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
   if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
@@ -245,6 +257,18 @@ MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_
   L.g.ld_y = ld_y;
   L.g.y_bf16 = (y_dtype == MXFP4_BF16);
   L.g.tiled = tiled;
+  const int64_t need = mxfp4::linear_small_workspace_bytes(m, n, k);
+  // the partial tiles are addressed with 32-bit byte offsets
+  if (need > 0 && (n > mxfp4::kLinearMaxN || need - mxfp4::kLinearCounterBytes >= (int64_t(1) << 31)))
+    return MXFP4_ERR_UNSUPPORTED;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MXFP4_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return MXFP4_ERR_UNSUPPORTED;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    L.counters = reinterpret_cast<uint32_t*>(ws);
+    L.partials = reinterpret_cast<float*>(ws + mxfp4::linear_small_counter_bytes(n));
+    L.ld_part = (n + 255) / 256 * 256;
+  }
   return from_hip(mxfp4::launch_linear_small(L, static_cast<hipStream_t>(stream)));
 }
 

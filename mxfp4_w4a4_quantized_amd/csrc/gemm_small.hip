@@ -131,12 +131,6 @@ __device__ __forceinline__ Operand operand(const uint8_t* codes, const uint8_t* 
   return o;
 }
 
-// Operand addressing with the layout chosen at run time (fused kernel).
-__device__ __forceinline__ Operand operand_rt(bool tiled, const uint8_t* codes, const uint8_t* scales, int row,
-                                              int rows, int k, int lg) {
-  return tiled ? operand<true>(codes, scales, row, rows, k, lg) : operand<false>(codes, scales, row, rows, k, lg);
-}
-
 // Tiled operands: the scale bytes of one K step of a 16-row fragment are 64
 // contiguous bytes (row-major [16][4]).  Lane (r, g) loads the dword of row r
 // for step s0 + 4 i + g, i.e. the scales of all four blocks of that step; the
@@ -368,23 +362,35 @@ void launch_mg(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Fused small-M linear layer: Y = Q(rot(X)) * W^T with the activation
-// quantization done inside the GEMM.  Lane (r, g) of a wave needs, for K step
-// s, the MX block 4 s + g of activation row r as its MFMA operand; it loads
-// those 32 elements itself, rotates and quantizes them with the quantizer's
-// own arithmetic (block_quant.h, so the codes equal the quantizer's bit for
-// bit) and feeds the codes and scale byte straight to the MFMA: quantized
-// activations never touch memory and there is no second launch.
+// quantization done inside the GEMM, one launch, no quantized activations in
+// memory (the rotation fused into the quantization and the matmul, as in
+// "Bridging the Gap Between Promise and Performance for Microscaling FP4
+// Quantization", "GPU Kernel Ondersteuning (QuTLASS)").
 //
-// Per chunk of KC steps a wave issues its activation loads (L2-resident: every
-// workgroup reads the same rows) before its weight loads, so it can rotate and
-// quantize while the weights stream in from HBM.  NG weight groups of 16 rows
-// per workgroup (32 rows for M <= 32) keep the redundant per-workgroup
-// quantization to N / (16 NG) copies; KC = 4 steps per wave keeps the
-// registers within two waves per SIMD.  Activations are bf16; the transform
-// is none, Hadamard-32, per-channel smoothing or a Kronecker product with
-// 2 <= P <= 16 (the factors sit in scalar registers; the degenerate 1 x 32 and
-// 32 x 1 forms, a dense 32 x 32 factor, are left to the separate quantizer).
-constexpr int KC = 4;          // K steps per fused chunk
+// Split over K.  Workgroup (grp, slice) takes LNR = 256 weight rows and a
+// slice of LKS = 8 K steps (1024 elements).  It first rotates and quantizes
+// the part of X that slice needs -- 16 MG rows x 32 blocks, one block per
+// thread and M group, with the quantizer's own arithmetic (block_quant.h, so
+// the codes equal the quantizer's bit for bit) -- into LDS, already in the
+// MFMA operand order.  Every block of X is then quantized by N / 256
+// workgroups instead of by every workgroup of a full-K split: for a Kronecker
+// transform (384 FMAs per block) that is what lets the arithmetic hide under
+// the weight stream.  The activation loads are issued before the weight
+// loads (vector memory completes in order) so the quantization runs while
+// the weights stream in.  The 8 waves then take 32 weight rows each over the
+// slice's steps, reading the quantized activations from LDS.
+//
+// With one slice the workgroup stores Y.  With S > 1 slices every workgroup
+// stores its fp32 partial tile into the workspace and counts itself on a
+// device-scope counter of its 256-row group; the last one to finish sums the
+// S partials in slice order (so Y does not depend on which workgroup
+// finishes last), stores Y, and sets the counter back to zero: the counters
+// are zero again whenever the kernel has completed.  The workspace holds
+// 4 S m * 256 ceil(n / 256) bytes of partials (the partial tiles' byte
+// offsets are 32-bit: below 2 GiB).
+constexpr int LNR = 256;      // weight rows per workgroup
+constexpr int LKS = 8;        // K steps per slice
+constexpr int LWAVES = 8;     // waves per workgroup, 32 weight rows each
 
 template <bool XBF16>
 struct RawBlock {
@@ -422,149 +428,210 @@ __device__ __forceinline__ void quantize_raw(const RawBlock<XBF16>& b, const flo
   codes = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int MG, int NG, bool XBF16, int ROT, int P, int Q>
-__global__ __launch_bounds__(64 * MAXW) void linear_small_kernel(LinearArgs L, int spw, int y_vec) {
-  static_assert(MG * NG <= MAXACC, "reduction buffer holds MAXACC tiles per wave");
-  static_assert(KC % 4 == 0, "dword scale loads cover 4 steps");
-  __shared__ v4f red[MAXW][MAXACC][64];
+template <int MG, int ROT, int P, int Q, bool TILED>
+__global__ __launch_bounds__(64 * LWAVES) void linear_small_kernel(LinearArgs L, int nslices, int y_vec) {
+  __shared__ u32x4 xq[MG][LKS][64];       // quantized activations, MFMA operand order
+  __shared__ uint8_t xsc[MG][LKS][64];    // their scale bytes
+  __shared__ int last_flag;
   const GemmArgs& g = L.g;
 
-  const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16 * NG;
+  const int grp = blockIdx.x, slice = blockIdx.y;
+  const int n0 = grp * LNR;
   const int kblocks = g.k >> 5;
   const int nsteps = (g.k + 127) >> 7;
-  const int s_begin = wave * spw;
-  const int s_end = min(nsteps, s_begin + spw);
-  const int64_t esz = XBF16 ? 2 : 4;
+  const int s0 = slice * LKS;
+  const int s_end = min(nsteps, s0 + LKS);
   const uint8_t* xb = static_cast<const uint8_t*>(L.x);
 
-  Operand w[NG];
+  // 1. the raw activation blocks this thread quantizes: block b = tid + 512 i
+  //    of the slice's [16 MG rows] x [32 block columns]
+  RawBlock<true> raw[MG];
 #pragma unroll
-  for (int q = 0; q < NG; ++q) w[q] = operand_rt(g.tiled, g.b_codes, g.b_scales, n0 + 16 * q + lr, g.n, g.k, lg);
-  // activation row of this lane in M group mg (rows past M quantize zeros)
-  const uint8_t* xrow[MG];
-  bool xin[MG];
-#pragma unroll
-  for (int mg = 0; mg < MG; ++mg) {
-    const int row = 16 * mg + lr;
-    xin[mg] = row < g.m;
-    xrow[mg] = xb + (int64_t)(xin[mg] ? row : 0) * L.ld_x * esz;
+  for (int i = 0; i < MG; ++i) {
+    const int b = tid + 64 * LWAVES * i;
+    const int row = b >> 5, col = 4 * s0 + (b & 31);
+    const bool ok = row < g.m && col < kblocks;
+    load_block<true>(xb + ((int64_t)(ok ? row : 0) * L.ld_x + (int64_t)(ok ? col : 0) * 32) * 2, ok, raw[i]);
   }
 
-  v4f acc[NG][MG];
+  // 2. this wave's weights: rows n0 + 32 wave + 16 f + lr over the slice's
+  //    steps, scales before codes.  Vector memory completes in order, so the
+  //    quantization below waits for the activation loads only and the scale
+  //    permutes for the scale loads only, while the code loads stream on.
+  //    Every lane issues the same loads whatever the shape: steps past the
+  //    slice or past K load from the slice's first step (always inside W) and
+  //    are zeroed afterwards, so the compiler's wait counts stay exact.
+  Operand w[2];
 #pragma unroll
-  for (int q = 0; q < NG; ++q)
+  for (int f = 0; f < 2; ++f)
+    w[f] = operand<TILED>(g.b_codes, g.b_scales, n0 + 32 * wave + 16 * f + lr, g.n, g.k, lg);
+  bool live[LKS];   // step s0 + j holds this lane's block
 #pragma unroll
-    for (int mg = 0; mg < MG; ++mg) acc[q][mg] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < LKS; ++j) live[j] = s0 + j < s_end && (TILED || 4 * (s0 + j) + lg < kblocks);
+  u32x4 wf[2][LKS];
+  int ws[2][LKS];
+  int wdw[2][LKS / 4];   // tiled: scale dwords, spread by permutes below
+  if constexpr (TILED) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int i4 = 0; i4 < LKS / 4; ++i4) {
+        const int st = min(s0 + 4 * i4 + lg, nsteps - 1);
+        wdw[f][i4] = *reinterpret_cast<const int*>(w[f].scale_row + (int64_t)st * w[f].sstride);
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < LKS; ++j)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) ws[f][j] = w[f].scale[(live[j] ? s0 + j : 0) * w[f].sstride - (live[j] ? 0 : lg)];
+  }
+#pragma unroll
+  for (int j = 0; j < LKS; ++j)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int64_t off = live[j] ? (s0 + j) * w[f].cstride : (TILED ? s0 * w[f].cstride : -16 * lg);
+      wf[f][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[f].code + off));
+    }
+  // keep every load above the quantization (the scheduler would sink them to
+  // their first use, after it)
+  __builtin_amdgcn_sched_barrier(0);
 
-  for (int s0 = s_begin; s0 < s_end; s0 += KC) {
-    u32x4 wf[NG][KC];
-    int ws[NG][KC];
+  // 3. rotate and quantize into LDS: block (row, c) of the slice is the
+  //    operand of lane (row % 16) + 16 (c % 4) at step c / 4, M group row / 16
+#pragma unroll
+  for (int i = 0; i < MG; ++i) {
+    const int b = tid + 64 * LWAVES * i;
+    const int row = b >> 5, c = b & 31;
+    const int col = min(4 * s0 + c, kblocks - 1);   // smoothing: this block's 32 factors
+    u32x4 codes;
+    int sb;
+    quantize_raw<true, ROT, P, Q>(raw[i], ROT == 3 ? L.fa + 32 * col : L.fa, L.fb, codes, sb);
+    xq[row >> 4][c >> 2][(row & 15) + 16 * (c & 3)] = codes;
+    xsc[row >> 4][c >> 2][(row & 15) + 16 * (c & 3)] = (uint8_t)sb;
+  }
+  if constexpr (TILED) {
+    // the scale of step s0 + 4 i + j for this lane's block lg is byte lg of
+    // lane (lr, j)'s dword i (see scales_dw)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int i4 = 0; i4 < LKS / 4; ++i4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ws[f][4 * i4 + j] = __shfl(wdw[f][i4], 16 * j + lr) >> (8 * lg);
+  }
+#pragma unroll
+  for (int j = 0; j < LKS; ++j)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      if (!live[j]) {
+        wf[f][j] = u32x4{0u, 0u, 0u, 0u};
+        ws[f][j] = 0;
+      }
+  __syncthreads();
+
+  // 4. MFMAs over the slice
+  v4f acc[2][MG];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) acc[f][mg] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < LKS; ++j)
+    if (s0 + j < s_end) {
+#pragma unroll
+      for (int mg = 0; mg < MG; ++mg) {
+        const u32x4 xf = xq[mg][j][lane];
+        const int xs = xsc[mg][j][lane];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) acc[f][mg] = mma(wf[f][j], xf, acc[f][mg], ws[f][j], xs);
+      }
+    }
+
+  // 5. lane holds Y[16 mg + lr][n0 + 32 wave + 16 f + 4 lg .. + 3] of this slice
+  if (nslices == 1) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int mg = 0; mg < MG; ++mg) {
+        const int m = 16 * mg + lr;
+        if (m < g.m) store4(g, m, n0 + 32 * wave + 16 * f + 4 * lg, acc[f][mg], y_vec);
+      }
+    return;
+  }
+  // Partial tiles go through device-coherent (sc1) stores, which write
+  // through this XCD's L2 to the memory side, and are read back with
+  // device-coherent loads: the same accesses as device-scope atomics, so no
+  // fence has to write back or invalidate whole caches (a release fence here,
+  // an L2 write-back per workgroup, cost more than the rest of the kernel).
+  // A wave's stores are complete once its store counter drains; the barrier
+  // then orders every wave's stores before the counter increment.
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(L.partials, 0, 0x7FFFFFFF, 0x00020000);
+  constexpr int kCoherent = 16;   // cache policy sc1: device scope
+  const int64_t slice_off = (int64_t)slice * g.m * L.ld_part;
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) {
-      // activation loads of this M group first: they do not wait behind the
-      // weight loads issued next
-      RawBlock<XBF16> raw[KC];
-#pragma unroll
-      for (int j = 0; j < KC; ++j) {
-        const int s = s0 + j, col = 4 * s + lg;
-        const bool ok = s < s_end && col < kblocks && xin[mg];
-        load_block<XBF16>(xrow[mg] + (int64_t)col * 32 * esz, ok, raw[j]);
-      }
-      if (mg == 0) {
-        // tiled weights with the whole chunk inside this wave's range: one
-        // scale dword per weight group instead of KC scale bytes (not with
-        // the Kronecker and smoothing transforms, whose registers are full)
-        const bool dws = ROT <= 1 && g.tiled && s0 + KC <= s_end;
-#pragma unroll
-        for (int j = 0; j < KC; ++j)
-#pragma unroll
-          for (int q = 0; q < NG; ++q) {
-            const int s = s0 + j;
-            wf[q][j] = u32x4{0u, 0u, 0u, 0u};
-            ws[q][j] = 0;
-            if (s < s_end && (g.tiled || 4 * s + lg < kblocks)) {
-              wf[q][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[q].code + s * w[q].cstride));
-              if (!dws) ws[q][j] = w[q].scale[s * w[q].sstride];
-            }
-          }
-        if (dws) {
-#pragma unroll
-          for (int q = 0; q < NG; ++q) scales_dw<KC>(w[q], s0, lane, ws[q]);
-        }
-      }
-      u32x4 xf[KC];
-      int xs[KC];
-#pragma unroll
-      for (int j = 0; j < KC; ++j) {
-        // smoothing: this lane's block column picks its 32 factors
-        const int col = min(4 * (s0 + j) + lg, kblocks - 1);
-        quantize_raw<XBF16, ROT, P, Q>(raw[j], ROT == 3 ? L.fa + 32 * col : L.fa, L.fb, xf[j], xs[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < KC; ++j)
-        if (s0 + j < s_end) {
-#pragma unroll
-          for (int q = 0; q < NG; ++q) acc[q][mg] = mma(wf[q][j], xf[j], acc[q][mg], ws[q][j], xs[j]);
-        }
-    }
-  }
-
-  if (nwaves > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int q = 0; q < NG; ++q)
-#pragma unroll
-        for (int mg = 0; mg < MG; ++mg) red[wave][q * MG + mg][lane] = acc[q][mg];
-    }
-    __syncthreads();
-    if (wave > 0) return;
-    for (int w2 = 1; w2 < nwaves; ++w2) {
-#pragma unroll
-      for (int q = 0; q < NG; ++q)
-#pragma unroll
-        for (int mg = 0; mg < MG; ++mg) acc[q][mg] += red[w2][q * MG + mg][lane];
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < NG; ++q)
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg) {
-      const int n = n0 + 16 * q + 4 * lg;
       const int m = 16 * mg + lr;
-      if (m >= g.m) continue;
-      store4(g, m, n, acc[q][mg], y_vec);
+      if (m < g.m) {
+        const int64_t e = slice_off + (int64_t)m * L.ld_part + n0 + 32 * wave + 16 * f + 4 * lg;
+        const v4f a = acc[f][mg];
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]), __float_as_uint(a[3])}, prs,
+            (int)(e * 4), 0, kCoherent);
+      }
     }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(L.counters + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = done == (uint32_t)(nslices - 1);
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  // the last workgroup of the group: the S tiles summed in slice order
+  const int chunks = g.m * (LNR / 4);
+  for (int c = tid; c < chunks; c += 64 * LWAVES) {
+    const int m = c / (LNR / 4), col = n0 + 4 * (c % (LNR / 4));
+    const int64_t e = (int64_t)m * L.ld_part + col;
+    v4f v = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < nslices; ++sl) {
+      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)((e + (int64_t)sl * g.m * L.ld_part) * 4), 0,
+                                                            kCoherent);
+      const v4f t = v4f{__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3])};
+      v = sl == 0 ? t : v + t;
+    }
+    store4(g, m, col, v, y_vec);
+  }
+  if (tid == 0) __hip_atomic_store(L.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MG, int NG, bool XBF16, int ROT, int P, int Q>
-void launch_fused(const LinearArgs& L, int nwaves, int spw, int y_vec, hipStream_t s) {
-  const int grid = (L.g.n + 16 * NG - 1) / (16 * NG);
-  linear_small_kernel<MG, NG, XBF16, ROT, P, Q><<<grid, 64 * nwaves, 0, s>>>(L, spw, y_vec);
+template <int MG, int ROT, int P, int Q>
+void launch_fused(const LinearArgs& L, int nslices, int y_vec, hipStream_t s) {
+  const dim3 grid((L.g.n + LNR - 1) / LNR, nslices);
+  if (L.g.tiled) linear_small_kernel<MG, ROT, P, Q, true><<<grid, 64 * LWAVES, 0, s>>>(L, nslices, y_vec);
+  else linear_small_kernel<MG, ROT, P, Q, false><<<grid, 64 * LWAVES, 0, s>>>(L, nslices, y_vec);
 }
 
-template <int MG, int NG, bool XBF16>
-hipError_t launch_fused_rot(const LinearArgs& L, int nwaves, int spw, int y_vec, hipStream_t s) {
-  if (L.rot == 0) launch_fused<MG, NG, XBF16, 0, 1, 32>(L, nwaves, spw, y_vec, s);
-  else if (L.rot == 1) launch_fused<MG, NG, XBF16, 1, 1, 32>(L, nwaves, spw, y_vec, s);
-  else if (L.rot == 3) launch_fused<MG, NG, XBF16, 3, 1, 32>(L, nwaves, spw, y_vec, s);
+template <int MG>
+hipError_t launch_fused_mg(const LinearArgs& L, int nslices, int y_vec, hipStream_t s) {
+  if (L.rot == 0) launch_fused<MG, 0, 1, 32>(L, nslices, y_vec, s);
+  else if (L.rot == 1) launch_fused<MG, 1, 1, 32>(L, nslices, y_vec, s);
+  else if (L.rot == 3) launch_fused<MG, 3, 1, 32>(L, nslices, y_vec, s);
   else {
     switch (L.p) {
-      case 2: launch_fused<MG, NG, XBF16, 2, 2, 16>(L, nwaves, spw, y_vec, s); break;
-      case 4: launch_fused<MG, NG, XBF16, 2, 4, 8>(L, nwaves, spw, y_vec, s); break;
-      case 8: launch_fused<MG, NG, XBF16, 2, 8, 4>(L, nwaves, spw, y_vec, s); break;
-      case 16: launch_fused<MG, NG, XBF16, 2, 16, 2>(L, nwaves, spw, y_vec, s); break;
+      case 2: launch_fused<MG, 2, 2, 16>(L, nslices, y_vec, s); break;
+      case 4: launch_fused<MG, 2, 4, 8>(L, nslices, y_vec, s); break;
+      case 8: launch_fused<MG, 2, 8, 4>(L, nslices, y_vec, s); break;
+      case 16: launch_fused<MG, 2, 16, 2>(L, nslices, y_vec, s); break;
       default: return hipErrorInvalidValue;
     }
   }
   return hipSuccess;
-}
-
-template <int MG, int NG>
-hipError_t launch_fused_mg(const LinearArgs& L, int nwaves, int spw, int y_vec, hipStream_t s) {
-  return launch_fused_rot<MG, NG, true>(L, nwaves, spw, y_vec, s);
 }
 
 }  // namespace
@@ -599,21 +666,32 @@ hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s) {
 
 namespace mxfp4 {
 
+int linear_small_slices(int64_t k) {
+  const int64_t nsteps = (k + 127) / 128;
+  return (int)((nsteps + LKS - 1) / LKS);
+}
+
+int64_t linear_small_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  const int nslices = linear_small_slices(k);
+  if (nslices <= 1) return 0;
+  const int64_t groups = (n + LNR - 1) / LNR;
+  return linear_small_counter_bytes(n) + (int64_t)nslices * m * groups * LNR * 4;
+}
+
+int64_t linear_small_counter_bytes(int64_t) { return kLinearCounterBytes; }
+
 hipError_t launch_linear_small(const LinearArgs& L, hipStream_t s) {
   if (!linear_small_supported(L)) return hipErrorInvalidValue;
-  const int nsteps = (L.g.k + 127) / 128;
-  int nwaves = (nsteps + KC - 1) / KC;
-  if (nwaves > MAXW) nwaves = MAXW;
-  if (nwaves < 1) nwaves = 1;
-  const int spw = (nsteps + nwaves - 1) / nwaves;
+  const int nslices = linear_small_slices(L.g.k);
+  if (nslices > 1 && (L.counters == nullptr || L.partials == nullptr)) return hipErrorInvalidValue;
   const size_t ybytes = L.g.y_bf16 ? 2 : 4;
   const int y_vec = (((uintptr_t)L.g.y) % (4 * ybytes) == 0) && (L.g.ld_y % 4 == 0);
   hipError_t e;
   switch ((L.g.m + 15) / 16) {
-    case 1: e = launch_fused_mg<1, 4>(L, nwaves, spw, y_vec, s); break;
-    case 2: e = launch_fused_mg<2, 2>(L, nwaves, spw, y_vec, s); break;
-    case 3: e = launch_fused_mg<3, 1>(L, nwaves, spw, y_vec, s); break;
-    default: e = launch_fused_mg<4, 1>(L, nwaves, spw, y_vec, s); break;
+    case 1: e = launch_fused_mg<1>(L, nslices, y_vec, s); break;
+    case 2: e = launch_fused_mg<2>(L, nslices, y_vec, s); break;
+    case 3: e = launch_fused_mg<3>(L, nslices, y_vec, s); break;
+    default: e = launch_fused_mg<4>(L, nslices, y_vec, s); break;
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();

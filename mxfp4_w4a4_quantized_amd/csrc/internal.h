@@ -72,8 +72,21 @@ struct LinearArgs {
   const float* fa;
   const float* fb;
   GemmArgs g;
+  // split over K (more than one slice of 1024 elements): per-group counters
+  // (zero between calls) and fp32 partial tiles [slices][m][ld_part]
+  uint32_t* counters = nullptr;
+  float* partials = nullptr;
+  int64_t ld_part = 0;   // ceil(n / 256) * 256
 };
 bool linear_small_supported(const LinearArgs& a);
 hipError_t launch_linear_small(const LinearArgs& a, hipStream_t s);
+// K slices of the fused layer, and the workspace it needs: a fixed region of
+// group counters (the same for every shape, so one workspace serves calls of
+// any shape) followed by the partial tiles; 0 for one slice.
+constexpr int64_t kLinearCounterBytes = 65536;             // 16384 groups of 256 weight rows
+constexpr int64_t kLinearMaxN = (kLinearCounterBytes / 4) * 256;
+int linear_small_slices(int64_t k);
+int64_t linear_small_counter_bytes(int64_t n);
+int64_t linear_small_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 }  // namespace mxfp4

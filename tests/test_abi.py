@@ -42,7 +42,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mx.lib().mxfp4_abi_version() == 2
+    assert mx.lib().mxfp4_abi_version() == 3
     for s in range(4):
         assert mx.status_string(s).startswith("MXFP4_")
     assert "unknown" in mx.status_string(99)
@@ -134,29 +134,54 @@ def test_linear_small_argument_errors():
     device access happens on any of these paths)."""
     INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
     A, R, T, BF, F = ALIGNED, mx.ROWMAJOR, mx.TILED, mx.MXFP4_BF16, mx.MXFP4_F32
-    assert ls(A, 7, 4, 64, 64, None, A, A, 8, R, A, F, 8, None) == INV    # bad x dtype
-    assert ls(A, BF, 4, 64, 64, None, A, A, 8, R, A, 9, 8, None) == INV   # bad y dtype
-    assert ls(A, BF, 4, 64, 64, None, A, A, 8, 2, A, F, 8, None) == INV   # bad layout
-    assert ls(A, BF, 4, 48, 64, None, A, A, 8, R, A, F, 8, None) == INV   # k % 32
-    assert ls(A, BF, 4, 64, 64, None, A, A, 8, T, A, F, 8, None) == INV   # tiled: k % 128
-    assert ls(A, BF, 4, 64, 32, None, A, A, 8, R, A, F, 8, None) == INV   # ld_x < k
-    assert ls(A, BF, 4, 64, 64, None, A, A, 8, R, A, F, 4, None) == INV   # ld_y < n
-    assert ls(A, BF, -1, 64, 64, None, A, A, 8, R, A, F, 8, None) == INV  # m < 0
-    assert ls(NULL, BF, 4, 64, 64, None, A, A, 8, R, A, F, 8, None) == INV
-    assert ls(A, BF, 4, 64, 64, None, NULL, A, 8, R, A, F, 8, None) == INV
-    assert ls(A, BF, 4, 64, 64, None, A, A, 8, R, NULL, F, 8, None) == INV
-    assert ls(NULL, BF, 0, 64, 64, None, NULL, NULL, 8, R, NULL, F, 8, None) == OK   # m == 0
-    assert ls(A, BF, 65, 64, 64, None, A, A, 8, R, A, F, 8, None) == UNS  # m > 64
-    assert ls(A, F, 4, 64, 64, None, A, A, 8, R, A, F, 8, None) == UNS    # fp32 activations
-    assert ls(MISALIGNED, BF, 4, 64, 64, None, A, A, 8, R, A, F, 8, None) == UNS
-    assert ls(A, BF, 4, 64, 68, None, A, A, 8, R, A, F, 8, None) == UNS   # row stride not 16 B
-    assert ls(A, BF, 4, 64, 64, None, A + 8, A, 8, R, A, F, 8, None) == UNS
-    assert ls(A, BF, 4, 128, 128, None, A, A + 2, 8, T, A, F, 8, None) == UNS   # tiled scales
+    assert ls(A, 7, 4, 64, 64, None, A, A, 8, R, A, F, 8, NULL, 0, None) == INV    # bad x dtype
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, R, A, 9, 8, NULL, 0, None) == INV   # bad y dtype
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, 2, A, F, 8, NULL, 0, None) == INV   # bad layout
+    assert ls(A, BF, 4, 48, 64, None, A, A, 8, R, A, F, 8, NULL, 0, None) == INV   # k % 32
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, T, A, F, 8, NULL, 0, None) == INV   # tiled: k % 128
+    assert ls(A, BF, 4, 64, 32, None, A, A, 8, R, A, F, 8, NULL, 0, None) == INV   # ld_x < k
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, R, A, F, 4, NULL, 0, None) == INV   # ld_y < n
+    assert ls(A, BF, -1, 64, 64, None, A, A, 8, R, A, F, 8, NULL, 0, None) == INV  # m < 0
+    assert ls(NULL, BF, 4, 64, 64, None, A, A, 8, R, A, F, 8, NULL, 0, None) == INV
+    assert ls(A, BF, 4, 64, 64, None, NULL, A, 8, R, A, F, 8, NULL, 0, None) == INV
+    assert ls(A, BF, 4, 64, 64, None, A, A, 8, R, NULL, F, 8, NULL, 0, None) == INV
+    assert ls(NULL, BF, 0, 64, 64, None, NULL, NULL, 8, R, NULL, F, 8, NULL, 0, None) == OK   # m == 0
+    assert ls(A, BF, 65, 64, 64, None, A, A, 8, R, A, F, 8, NULL, 0, None) == UNS  # m > 64
+    assert ls(A, F, 4, 64, 64, None, A, A, 8, R, A, F, 8, NULL, 0, None) == UNS    # fp32 activations
+    assert ls(MISALIGNED, BF, 4, 64, 64, None, A, A, 8, R, A, F, 8, NULL, 0, None) == UNS
+    assert ls(A, BF, 4, 64, 68, None, A, A, 8, R, A, F, 8, NULL, 0, None) == UNS   # row stride not 16 B
+    assert ls(A, BF, 4, 64, 64, None, A + 8, A, 8, R, A, F, 8, NULL, 0, None) == UNS
+    assert ls(A, BF, 4, 128, 128, None, A, A + 2, 8, T, A, F, 8, NULL, 0, None) == UNS   # tiled scales
     for p_, q_ in ((1, 32), (32, 1)):
         kr = mx.RotationDesc(mx.ROT_KRON, p_, q_, 0, A, A)
-        assert ls(A, BF, 4, 64, 64, ctypes.byref(kr), A, A, 8, R, A, F, 8, None) == UNS
+        assert ls(A, BF, 4, 64, 64, ctypes.byref(kr), A, A, 8, R, A, F, 8, NULL, 0, None) == UNS
     kr = mx.RotationDesc(mx.ROT_KRON, 4, 4, 0, A, A)
-    assert ls(A, BF, 4, 64, 64, ctypes.byref(kr), A, A, 8, R, A, F, 8, None) == INV   # p*q != 32
+    assert ls(A, BF, 4, 64, 64, ctypes.byref(kr), A, A, 8, R, A, F, 8, NULL, 0, None) == INV   # p*q != 32
+
+
+def test_linear_small_workspace():
+    """Workspace size of the fused layer: none for one K slice (k <= 1024),
+    else 64 KiB of group counters plus the fp32 partial tiles; a missing or
+    short workspace is rejected synchronously."""
+    INV, UNS = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED
+    A, T, BF, F = ALIGNED, mx.TILED, mx.MXFP4_BF16, mx.MXFP4_F32
+    b = ctypes.c_int64()
+    W = mx.lib().mxfp4_linear_small_workspace
+    assert mx.linear_small_workspace_bytes(16, 14336, 1024) == 0
+    groups = 14336 // 256
+    assert mx.linear_small_workspace_bytes(16, 14336, 4096) == 65536 + 4 * 16 * groups * 256 * 4
+    assert mx.linear_small_workspace_bytes(1, 300, 4128) == 65536 + 5 * 1 * 512 * 4
+    assert W(1, (1 << 22) + 1, 2048, ctypes.byref(b)) == UNS          # more than 16384 counters
+    assert mx.linear_small_workspace_bytes(0, 300, 4096) == 0
+    assert W(65, 300, 4096, ctypes.byref(b)) == UNS
+    assert W(64, 1 << 24, 8192, ctypes.byref(b)) == UNS              # partial tiles past 2 GiB
+    assert ls(A, BF, 64, 8192, 8192, None, A, A, 1 << 24, T, A, F, 1 << 24, A, 1 << 40, None) == UNS
+    assert W(4, 300, 48, ctypes.byref(b)) == INV
+    assert W(4, 300, 64, None) == INV
+    need = mx.linear_small_workspace_bytes(16, 512, 4096)
+    assert ls(A, BF, 16, 4096, 4096, None, A, A, 512, T, A, F, 512, NULL, 0, None) == INV        # missing
+    assert ls(A, BF, 16, 4096, 4096, None, A, A, 512, T, A, F, 512, A, need - 4, None) == INV    # short
+    assert ls(A, BF, 16, 4096, 4096, None, A, A, 512, T, A, F, 512, A + 16, need, None) == UNS   # alignment
 
 
 def test_gemm_requant_argument_errors():

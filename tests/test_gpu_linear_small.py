@@ -185,3 +185,53 @@ def test_fused_unsupported_cases_raise():
     x = torch.zeros((65, 64), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(mx.Mxfp4Error):
         mx.linear_small(x, wc, ws)                               # m > 64
+
+
+@pytest.mark.parametrize("m,n,k,rot", [(16, 3000, 4096, (4, 8)), (64, 700, 12288, "h32"), (5, 256, 2048, None)],
+                         ids=str)
+def test_split_k_workspace_contract(m, n, k, rot):
+    """Split over K (k > 1024): with a caller-supplied zeroed workspace, two
+    calls in a row give bit-identical Y (the partial tiles are summed in slice
+    order whichever workgroup finishes last), every group counter is back at
+    zero after each call, and Y meets the oracle bound."""
+    rng = np.random.default_rng(m + n + k)
+    x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
+    wc, ws = workloads.random_mxfp4(rng, n, k)
+    r = make_rot(rot, k=k)
+    need = mx.linear_small_workspace_bytes(m, n, k)
+    groups = -(-n // 256)
+    assert need > 65536
+    work = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    dwc, dws = weights_dev(wc, ws, mx.TILED)
+    announce("linear_small split-k workspace", m, n, k, rot)
+    xd = bf16_dev(x)
+    y1 = mx.linear_small(xd, dwc, dws, r, torch.float32, layout=mx.TILED, n=n, workspace=work)
+    torch.cuda.synchronize()
+    assert not work[:4 * groups].any(), "group counters not reset"
+    y2 = mx.linear_small(xd, dwc, dws, r, torch.float32, layout=mx.TILED, n=n, workspace=work)
+    torch.cuda.synchronize()
+    assert not work[:4 * groups].any(), "group counters not reset"
+    assert torch.equal(y1, y2)
+    xc, xs = oracle.quantize(x, rot=oracle_rot(r), bf16=True)
+    ref = oracle.gemm(xc, xs, wc, ws)
+    assert norm_err(y1.cpu().numpy(), ref, row_norms(xc, xs), row_norms(wc, ws)) <= TOL
+
+
+def test_split_k_workspace_reused_across_shapes():
+    """One workspace serves calls of different shapes in stream order: the
+    counter region is the same for every shape and each call leaves it zero."""
+    shapes = [(16, 3000, 4096), (7, 9000, 2048), (33, 500, 8192), (16, 3000, 4096)]
+    need = max(mx.linear_small_workspace_bytes(m, n, k) for m, n, k in shapes)
+    work = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for i, (m, n, k) in enumerate(shapes):
+        rng = np.random.default_rng(400 + i)
+        x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
+        wc, ws = workloads.random_mxfp4(rng, n, k)
+        announce("linear_small shared workspace", m, n, k)
+        dwc, dws = weights_dev(wc, ws, mx.TILED)
+        y = mx.linear_small(bf16_dev(x), dwc, dws, "h32", torch.float32, layout=mx.TILED, n=n, workspace=work)
+        torch.cuda.synchronize()
+        assert not work[:65536].any(), "counters not reset"
+        xc, xs = oracle.quantize(x, rot="h32", bf16=True)
+        ref = oracle.gemm(xc, xs, wc, ws)
+        assert norm_err(y.cpu().numpy(), ref, row_norms(xc, xs), row_norms(wc, ws)) <= TOL
