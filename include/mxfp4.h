@@ -257,6 +257,26 @@ MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_
                                           int32_t layout, void* y, int32_t y_dtype, int64_t ld_y,
                                           void* workspace, int64_t workspace_bytes, void* stream);
 
+/* mxfp4_linear_small for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and result as mxfp4_linear_small without the
+ * workspace: the split over K uses a fixed 16 MiB array of device memory
+ * inside the library instead (one per GPU, held until the process ends; its
+ * counters are cleared by the first call on each device).  The call
+ * allocates nothing.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (other streams, other host threads) race:
+ * serialize them, or give each its own workspace with mxfp4_linear_small.
+ * Limit: mxfp4_linear_small_workspace(m, n, k) <= 16 MiB (for m = 16 and
+ * k = 4096, n <= 65280).
+ * Errors: as mxfp4_linear_small, and UNSUPPORTED past that limit (checked
+ *   before anything is launched); HIP if the scratch address lookup or a
+ *   launch fails. */
+MXFP4_API mxfp4_status mxfp4_linear_small_noalloc(const void* x, int32_t x_dtype, int64_t m, int64_t k,
+                                                  int64_t ld_x, const mxfp4_rotation* rot,
+                                                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t n,
+                                                  int32_t layout, void* y, int32_t y_dtype, int64_t ld_y,
+                                                  void* stream);
+
 /* Workspace size of mxfp4_linear_small for (m, n, k): 0 when k <= 1024 (one
  * K slice), else 64 KiB of group counters plus ceil(k / 1024) fp32 partial
  * tiles of m x 256 ceil(n / 256).  The fused layer over 16 x 4096 -> 14336

@@ -46,7 +46,8 @@ TILE_ROWS, TILE_K = 256, 128
 HADAMARD32 = "h32"
 
 EXPORTED = ("mxfp4_quantize_rotate", "mxfp4_quantize_fit", "mxfp4_gemm", "mxfp4_gemm_requant",
-            "mxfp4_linear_small", "mxfp4_linear_small_workspace", "mxfp4_tiled_bytes",
+            "mxfp4_linear_small", "mxfp4_linear_small_noalloc", "mxfp4_linear_small_workspace",
+            "mxfp4_tiled_bytes",
             "mxfp4_inverse_transpose", "mxfp4_smooth_weight_factors", "mxfp4_status_string",
             "mxfp4_abi_version")
 LINEAR_SMALL_MAX_M = 64
@@ -87,6 +88,9 @@ def lib() -> ctypes.CDLL:
     L.mxfp4_linear_small.restype = i32
     L.mxfp4_linear_small.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), vp, vp, i64, i32,
                                      vp, i32, i64, vp, i64, vp]
+    L.mxfp4_linear_small_noalloc.restype = i32
+    L.mxfp4_linear_small_noalloc.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(RotationDesc), vp, vp, i64,
+                                             i32, vp, i32, i64, vp]
     L.mxfp4_linear_small_workspace.restype = i32
     L.mxfp4_linear_small_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
     L.mxfp4_tiled_bytes.restype = i32
@@ -386,6 +390,35 @@ def linear_small(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
         workspace.data_ptr() if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, stream)
     _check(st, "mxfp4_linear_small")
+    return y
+
+
+def linear_small_noalloc(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, y: torch.Tensor,
+                         rot=None, layout: int = ROWMAJOR) -> torch.Tensor:
+    """linear_small for callers that cannot allocate: the split over K uses
+    the library's fixed 16 MiB per-GPU scratch (mxfp4_linear_small_noalloc);
+    y [m, n] is the caller's.  Calls that overlap in time on one GPU share
+    that scratch and race."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    m, k = x.shape
+    _on_device(x.device, w_codes=w_codes, w_scales=w_scales, y=y)
+    desc, _keep = _rot_desc(rot, x.device, k)
+    if y.dim() != 2 or y.shape[0] != m or y.stride(1) != 1:
+        raise ValueError("y must be [m, n] with unit column stride")
+    n = y.shape[1]
+    cshape, sshape = _out_shapes(n, k, layout)
+    if tuple(w_codes.shape) != cshape or tuple(w_scales.shape) != sshape:
+        raise ValueError(f"weights: codes/scales must be {cshape} / {sshape}")
+    for t in (w_codes, w_scales):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("codes and scales must be contiguous uint8 tensors")
+    st = lib().mxfp4_linear_small_noalloc(
+        x.data_ptr(), _dtype_code(x.dtype), m, k, x.stride(0),
+        ctypes.byref(desc) if desc is not None else None,
+        w_codes.data_ptr(), w_scales.data_ptr(), n, layout,
+        y.data_ptr(), _dtype_code(y.dtype), y.stride(0), _stream(x.device))
+    _check(st, "mxfp4_linear_small_noalloc")
     return y
 
 

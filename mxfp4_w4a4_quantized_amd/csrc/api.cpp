@@ -213,11 +213,16 @@ MXFP4_API mxfp4_status mxfp4_linear_small_workspace(int64_t m, int64_t n, int64_
   return MXFP4_OK;
 }
 
-MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t ld_x,
-                                          const mxfp4_rotation* rot, const uint8_t* w_codes,
-                                          const uint8_t* w_scales, int64_t n, int32_t layout, void* y,
-                                          int32_t y_dtype, int64_t ld_y, void* workspace,
-                                          int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch of the fused layer; ws == nullptr with
+// use_static selects the library's fixed scratch.
+mxfp4_status linear_small_impl(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t ld_x,
+                               const mxfp4_rotation* rot, const uint8_t* w_codes, const uint8_t* w_scales,
+                               int64_t n, int32_t layout, void* y, int32_t y_dtype, int64_t ld_y, void* workspace,
+                               int64_t workspace_bytes, bool use_static, void* stream) {
   if (x_dtype != MXFP4_F32 && x_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
   if (y_dtype != MXFP4_F32 && y_dtype != MXFP4_BF16) return MXFP4_ERR_INVALID_ARG;
   if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_TILED) return MXFP4_ERR_INVALID_ARG;
@@ -236,6 +241,11 @@ MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_
   if (tiled && !aligned(w_scales, 4)) return MXFP4_ERR_UNSUPPORTED;
   const int64_t ybytes = (y_dtype == MXFP4_BF16) ? 2 : 4;
   if (!aligned(y, ybytes)) return MXFP4_ERR_UNSUPPORTED;
+  const int64_t need = mxfp4::linear_small_workspace_bytes(m, n, k);
+  // the partial tiles are addressed with 32-bit byte offsets
+  if (need > 0 && (n > mxfp4::kLinearMaxN || need - mxfp4::kLinearCounterBytes >= (int64_t(1) << 31)))
+    return MXFP4_ERR_UNSUPPORTED;
+  if (use_static && need > mxfp4::kLinearStaticScratchBytes) return MXFP4_ERR_UNSUPPORTED;
 
   mxfp4::LinearArgs L;
   L.x = x;
@@ -257,19 +267,41 @@ MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_
   L.g.ld_y = ld_y;
   L.g.y_bf16 = (y_dtype == MXFP4_BF16);
   L.g.tiled = tiled;
-  const int64_t need = mxfp4::linear_small_workspace_bytes(m, n, k);
-  // the partial tiles are addressed with 32-bit byte offsets
-  if (need > 0 && (n > mxfp4::kLinearMaxN || need - mxfp4::kLinearCounterBytes >= (int64_t(1) << 31)))
-    return MXFP4_ERR_UNSUPPORTED;
   if (need > 0) {
+    if (use_static) {
+      const hipError_t e = mxfp4::linear_small_static_scratch(&workspace, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return MXFP4_ERR_HIP;
+      workspace_bytes = mxfp4::kLinearStaticScratchBytes;
+    }
     if (workspace == nullptr || workspace_bytes < need) return MXFP4_ERR_INVALID_ARG;
     if (!aligned(workspace, 256)) return MXFP4_ERR_UNSUPPORTED;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     L.counters = reinterpret_cast<uint32_t*>(ws);
-    L.partials = reinterpret_cast<float*>(ws + mxfp4::linear_small_counter_bytes(n));
+    L.partials = reinterpret_cast<float*>(ws + mxfp4::kLinearCounterBytes);
     L.ld_part = (n + 255) / 256 * 256;
   }
   return from_hip(mxfp4::launch_linear_small(L, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t ld_x,
+                                          const mxfp4_rotation* rot, const uint8_t* w_codes,
+                                          const uint8_t* w_scales, int64_t n, int32_t layout, void* y,
+                                          int32_t y_dtype, int64_t ld_y, void* workspace,
+                                          int64_t workspace_bytes, void* stream) {
+  return linear_small_impl(x, x_dtype, m, k, ld_x, rot, w_codes, w_scales, n, layout, y, y_dtype, ld_y, workspace,
+                           workspace_bytes, false, stream);
+}
+
+MXFP4_API mxfp4_status mxfp4_linear_small_noalloc(const void* x, int32_t x_dtype, int64_t m, int64_t k,
+                                                  int64_t ld_x, const mxfp4_rotation* rot, const uint8_t* w_codes,
+                                                  const uint8_t* w_scales, int64_t n, int32_t layout, void* y,
+                                                  int32_t y_dtype, int64_t ld_y, void* stream) {
+  return linear_small_impl(x, x_dtype, m, k, ld_x, rot, w_codes, w_scales, n, layout, y, y_dtype, ld_y, nullptr, 0,
+                           true, stream);
 }
 
 // Reciprocals of the activation-side smoothing factors, for the weight fold:

@@ -46,6 +46,8 @@
 #include "internal.h"
 #include "block_quant.h"
 
+#include <mutex>
+
 namespace mxfp4 {
 namespace {
 
@@ -665,6 +667,44 @@ hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s) {
 }  // namespace mxfp4
 
 namespace mxfp4 {
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch for mxfp4_linear_small_noalloc, the fused layer for
+// callers that cannot allocate: the workspace of the split over K lives in
+// this array, one copy per GPU, held until the process ends.  Host code never
+// uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[kLinearStaticScratchBytes];
+
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t linear_small_static_scratch(void** ptr, hipStream_t s) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    // the counters start at zero (a fill kernel, not a memset node, in case
+    // the first call is captured into a graph); later calls leave them zero
+    constexpr int words = (int)(kLinearCounterBytes / 4);
+    clear_words_kernel<<<(words + 255) / 256, 256, 0, s>>>(static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 int linear_small_slices(int64_t k) {
   const int64_t nsteps = (k + 127) / 128;

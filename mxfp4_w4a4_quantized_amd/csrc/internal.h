@@ -86,6 +86,11 @@ hipError_t launch_linear_small(const LinearArgs& a, hipStream_t s);
 constexpr int64_t kLinearCounterBytes = 65536;             // 16384 groups of 256 weight rows
 constexpr int64_t kLinearMaxN = (kLinearCounterBytes / 4) * 256;
 int linear_small_slices(int64_t k);
+// The fixed scratch of the allocation-free variant: its device address on
+// the current device (looked up, and its counters cleared on `s`, on the
+// first call per device).
+constexpr int64_t kLinearStaticScratchBytes = int64_t(16) << 20;
+hipError_t linear_small_static_scratch(void** ptr, hipStream_t s);
 int64_t linear_small_counter_bytes(int64_t n);
 int64_t linear_small_workspace_bytes(int64_t m, int64_t n, int64_t k);
 

@@ -184,6 +184,20 @@ def test_linear_small_workspace():
     assert ls(A, BF, 16, 4096, 4096, None, A, A, 512, T, A, F, 512, A + 16, need, None) == UNS   # alignment
 
 
+def test_linear_small_noalloc_rejects_before_any_device_work():
+    """The allocation-free fused layer checks its arguments and its 16 MiB
+    scratch limit synchronously, before looking up or touching the scratch."""
+    INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
+    A, T, BF, F = ALIGNED, mx.TILED, mx.MXFP4_BF16, mx.MXFP4_F32
+    na = mx.lib().mxfp4_linear_small_noalloc
+    assert mx.linear_small_workspace_bytes(16, 65536, 4096) > 16 << 20
+    assert na(A, BF, 16, 4096, 4096, None, A, A, 65536, T, A, F, 65536, None) == UNS     # past 16 MiB
+    assert na(A, BF, 64, 8192, 8192, None, A, A, 14336, T, A, F, 14336, None) == UNS     # past 16 MiB
+    assert na(A, BF, 65, 4096, 4096, None, A, A, 512, T, A, F, 512, None) == UNS         # m > 64
+    assert na(A, BF, 16, 4096, 4096, None, NULL, A, 512, T, A, F, 512, None) == INV      # null weights
+    assert na(NULL, BF, 0, 4096, 4096, None, NULL, NULL, 512, T, NULL, F, 512, None) == OK   # m == 0
+
+
 def test_gemm_requant_argument_errors():
     INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
     A, R, T = ALIGNED, mx.ROWMAJOR, mx.TILED
