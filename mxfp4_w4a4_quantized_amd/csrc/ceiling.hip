@@ -1,4 +1,6 @@
-// Measurement kernel, not part of the MXFP4 path: the rate at which this
+// Measurement kernels, not part of the MXFP4 path.
+//
+// mxfp4_ceiling_mfma: the rate at which this
 // device sustains the block-scaled FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4,
 // E2M1 operands, one E8M0 byte per 32-element block, as the large GEMM issues
 // it) when every SIMD of every CU issues it back to back, with no memory
@@ -10,6 +12,15 @@
 // wave keeps 8 independent accumulators (no MFMA waits on another's result)
 // and cycles through 4 A and 4 B operand registers filled with pseudo-random
 // codes and per-MFMA scale bytes, so the operands toggle like real data.
+//
+// mxfp4_ceiling_stream: the HBM rate of a bare streaming kernel with the
+// memory pattern of the quantizer and of the decode GEMM and no arithmetic:
+// each wave reads `rk` KiB (one KiB per load instruction, 16 contiguous
+// bytes per lane, non-temporal) and writes `wk` KiB (wk <= rk) the same way:
+// with rk = 4 a wave's KiB are contiguous (the quantizer's pattern), with
+// rk = 16 its loads are spread over the buffer (the decode GEMM's).
+// Its time over the same byte counts is the practical ceiling of a kernel of
+// that size: launch, ramp and drain included.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -70,7 +81,62 @@ __global__ __launch_bounds__(256, 1) void mfma_loop(float* out, unsigned long lo
   if (lane == 0) cycles[blockIdx.x * 4 + wave] = (unsigned long long)(t1 - t0);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// STRIDED: load i of wave w takes KiB i * waves + w, so every load
+// instruction of the grid sweeps the buffer in step (the decode GEMM's waves
+// read one KiB from each of several 16 KiB stage blocks); else the wave's
+// rk KiB are contiguous (the quantizer's waves).
+template <int RK, bool STRIDED>
+__global__ __launch_bounds__(256) void stream_loop(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                    int64_t waves, int wk) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave >= waves) return;
+  u32x4 v[RK];
+#pragma unroll
+  for (int i = 0; i < RK; ++i)
+    v[i] = __builtin_nontemporal_load(src + (STRIDED ? (i * waves + wave) : (wave * RK + i)) * 64 + lane);
+  u32x4* d = dst + wave * wk * 64 + lane;
+  for (int i = 0; i < wk; ++i) {   // each store carries data of every load
+    u32x4 x = v[i];
+#pragma unroll
+    for (int j = 0; j < RK; ++j) x ^= j == i ? u32x4{0u, 0u, 0u, 0u} : v[j];
+    __builtin_nontemporal_store(x, d + 64 * i);
+  }
+  if (wk == 0) {   // keep the loads live: a store that never happens in practice
+    u32x4 x = v[0];
+#pragma unroll
+    for (int j = 1; j < RK; ++j) x ^= v[j];
+    if (x[0] == 0x9e3779b9u && x[1] == 0x7f4a7c15u && x[2] == 0x12345678u && x[3] == 0xdeadbeefu) dst[lane] = x;
+  }
+}
+
 }  // namespace
+
+// waves waves of 64 lanes (4 per workgroup); wave w reads rk KiB of src (KiB
+// rk w .. rk w + rk - 1 for rk = 4 or 8, KiB i waves + w for i < 16 when rk =
+// 16) and writes KiB wk w .. wk w + wk - 1 of dst (0 <= wk <= rk; dst at
+// least 1 KiB when wk == 0).  src holds waves * rk
+// KiB, dst waves * max(wk, 1) KiB, both 16-byte aligned device memory.
+// Returns 0, or a HIP error code.
+extern "C" __attribute__((visibility("default"))) int mxfp4_ceiling_stream(const void* src, void* dst, long long waves,
+                                                                             int rk, int wk, void* stream) {
+  if (src == nullptr || dst == nullptr || waves <= 0 || wk < 0 || wk > rk || ((uintptr_t)src % 16) != 0 ||
+      ((uintptr_t)dst % 16) != 0)
+    return (int)hipErrorInvalidValue;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const u32x4* a = static_cast<const u32x4*>(src);
+  u32x4* b = static_cast<u32x4*>(dst);
+  switch (rk) {
+    case 4: stream_loop<4, false><<<grid, block, 0, s>>>(a, b, waves, wk); break;
+    case 8: stream_loop<8, false><<<grid, block, 0, s>>>(a, b, waves, wk); break;
+    case 16: stream_loop<16, true><<<grid, block, 0, s>>>(a, b, waves, wk); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
 
 // blocks workgroups (use the CU count), iters rounds of 8 MFMAs per wave (a
 // multiple of 4).

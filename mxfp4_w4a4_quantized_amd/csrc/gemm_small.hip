@@ -39,7 +39,11 @@
 //    never stored); blocks beyond K are zero codes with a zero scale byte, so
 //    a K tail contributes exactly 0.
 //  * M is covered in groups of 16 rows that reuse the weight fragments held
-//    in registers.
+//    in registers; past 64 rows, one grid row per 64 activation rows.  That
+//    serves the small shapes too (fewer output tiles of 256 x 256 than the
+//    chip has XCDs), where one large tile per workgroup would run a handful
+//    of workgroups through a whole load ring and epilogue while the rest of
+//    the chip idles.
 //  * A wave whose chunk of steps lies wholly inside K issues its loads with
 //    no predicates, so the waits before the MFMAs can count them down one by
 //    one; only a K tail takes the predicated path.
@@ -207,6 +211,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * 16 * NG;
+  const int m0 = blockIdx.y * 16 * MAXMG;   // M beyond 64 rows: one grid row per 64 activation rows
   const int kblocks = g.k >> 5;
   const int nsteps = (g.k + 127) >> 7;
   const int s_begin = wave * spw;
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
   for (int q = 0; q < NG; ++q) w[q] = operand<TILED>(g.b_codes, g.b_scales, n0 + 16 * q + lr, g.n, g.k, lg);
   Operand x[MG];
 #pragma unroll
-  for (int mg = 0; mg < MG; ++mg) x[mg] = operand<TILED>(g.a_codes, g.a_scales, 16 * mg + lr, g.m, g.k, lg);
+  for (int mg = 0; mg < MG; ++mg) x[mg] = operand<TILED>(g.a_codes, g.a_scales, m0 + 16 * mg + lr, g.m, g.k, lg);
 
   v4f acc[NG][MG];
 #pragma unroll
@@ -307,16 +312,16 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
 
   if constexpr (OUT == 2) {
 #pragma unroll
-    for (int mg = 0; mg < MG; ++mg) store_requant(g, 16 * mg + lr, n0, acc[0][mg], acc[NG - 1][mg], lane);
+    for (int mg = 0; mg < MG; ++mg) store_requant(g, m0 + 16 * mg + lr, n0, acc[0][mg], acc[NG - 1][mg], lane);
     return;
   }
-  // lane holds Y[16 mg + lr][n .. n + 3] of weight group q
+  // lane holds Y[m0 + 16 mg + lr][n .. n + 3] of weight group q
 #pragma unroll
   for (int q = 0; q < NG; ++q)
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) {
       const int n = n0 + 16 * q + 4 * lg;
-      const int m = 16 * mg + lr;
+      const int m = m0 + 16 * mg + lr;
       if (m >= g.m) continue;
       const v4f v = acc[q][mg];
       if constexpr (BF16OUT) {
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
 
 template <int MG, int NG, int OUT, bool TILED>
 void launch(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s) {
-  const int grid = (g.n + 16 * NG - 1) / (16 * NG);
+  const dim3 grid((g.n + 16 * NG - 1) / (16 * NG), (g.m + 16 * MAXMG - 1) / (16 * MAXMG));
   gemm_small_kernel<MG, NG, OUT, TILED><<<grid, 64 * nwaves, 0, s>>>(g, spw, y_vec);
 }
 
@@ -638,12 +643,21 @@ hipError_t launch_fused_mg(const LinearArgs& L, int nslices, int y_vec, hipStrea
 
 }  // namespace
 
+// The small-M kernel takes decode shapes (m <= 64) and shapes with fewer
+// 256 x 256 output tiles than the chip has XCDs (8), where the large-tile
+// kernel would run a handful of workgroups through its whole load ring and
+// epilogue while the rest of the chip idles; here each workgroup takes 32
+// (16) weight rows and 64 activation rows.
+bool gemm_small_route(int64_t m, int64_t n) {
+  return m >= 1 && (m <= 16 * MAXMG || ((m + 255) / 256) * ((n + 255) / 256) < 8);
+}
+
 bool gemm_small_supported(const GemmArgs& g) {
-  return g.m >= 1 && g.m <= 16 * MAXMG && (!g.q_out || (g.n % (g.q_tiled ? 128 : 32)) == 0);
+  return gemm_small_route(g.m, g.n) && (!g.q_out || (g.n % (g.q_tiled ? 128 : 32)) == 0);
 }
 
 bool linear_small_supported(const LinearArgs& L) {
-  return gemm_small_supported(L.g) && L.x_bf16 && (L.rot != 2 || (L.p >= 2 && L.p <= 16));
+  return L.g.m >= 1 && L.g.m <= 16 * MAXMG && L.x_bf16 && (L.rot != 2 || (L.p >= 2 && L.p <= 16));
 }
 
 hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s) {
@@ -655,7 +669,7 @@ hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s) {
   const int spw = (nsteps + nwaves - 1) / nwaves;
   const size_t ybytes = g.y_bf16 ? 2 : 4;
   const int y_vec = (((uintptr_t)g.y) % (4 * ybytes) == 0) && (g.ld_y % 4 == 0);
-  switch ((g.m + 15) / 16) {
+  switch (g.m > 16 * MAXMG ? MAXMG : (g.m + 15) / 16) {
     case 1: launch_mg<1, 2>(g, nwaves, spw, y_vec, s); break;
     case 2: launch_mg<2, 2>(g, nwaves, spw, y_vec, s); break;
     case 3: launch_mg<3, 1>(g, nwaves, spw, y_vec, s); break;

@@ -54,8 +54,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 bool gemm_large_supported(const GemmArgs& a);
 hipError_t launch_gemm_large(const GemmArgs& a, hipStream_t s);
 
-// Small-M kernel (gemm_small.hip): 1 <= m <= 64, either layout; the kernel
-// for decode shapes, bound by streaming the weights from HBM.
+// Small-M kernel (gemm_small.hip): either layout; the kernel for decode
+// shapes (m <= 64), bound by streaming the weights from HBM, and for shapes
+// with fewer than 8 output tiles of 256 x 256 (gemm_small_route).
+bool gemm_small_route(int64_t m, int64_t n);
 bool gemm_small_supported(const GemmArgs& a);
 hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t s);
 

@@ -361,9 +361,16 @@ def test_measurement_library_loads_and_rejects_bad_arguments():
     from mxfp4_w4a4_quantized_amd import build as hip_build
     L = ctypes.CDLL(hip_build.CEILING_LIB)
     out = os.popen(f"nm -D --defined-only {hip_build.CEILING_LIB}").read()
-    assert set(re.findall(r"\bT (\w+)", out)) == {"mxfp4_ceiling_mfma"}
+    assert set(re.findall(r"\bT (\w+)", out)) == {"mxfp4_ceiling_mfma", "mxfp4_ceiling_stream"}
     L.mxfp4_ceiling_mfma.restype = ctypes.c_int
     L.mxfp4_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     for blocks, iters, o, c in ((0, 4, ALIGNED, ALIGNED), (4, 0, ALIGNED, ALIGNED), (4, 6, ALIGNED, ALIGNED),
                                 (4, 4, NULL, ALIGNED), (4, 4, ALIGNED, NULL)):
         assert L.mxfp4_ceiling_mfma(blocks, iters, o, c, NULL) != 0
+    L.mxfp4_ceiling_stream.restype = ctypes.c_int
+    L.mxfp4_ceiling_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p]
+    for src, dst, waves, rk, wk in ((NULL, ALIGNED, 8, 4, 1), (ALIGNED, NULL, 8, 4, 1), (ALIGNED, ALIGNED, 0, 4, 1),
+                                    (ALIGNED, ALIGNED, 8, 5, 1), (ALIGNED, ALIGNED, 8, 4, 5),
+                                    (ALIGNED, ALIGNED, 8, 4, -1), (ALIGNED + 8, ALIGNED, 8, 4, 1)):
+        assert L.mxfp4_ceiling_stream(src, dst, waves, rk, wk, NULL) != 0

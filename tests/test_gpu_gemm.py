@@ -91,13 +91,15 @@ def test_random_operands(m, n, k):
     check_full(ac, as_, bc, bs, "random")
 
 
-# Shapes for the large-tile persistent kernel (K a multiple of 128, M > 64):
-# one K stage, fewer stages than the load ring, ragged M and N, fewer tiles
-# than CUs (grid not a multiple of 8), and more tiles than CUs (several tiles
-# per workgroup, the load ring running across tile boundaries).
+# Shapes for the large-tile persistent kernel (K a multiple of 128, M > 64,
+# at least 8 output tiles of 256 x 256; fewer tiles go to the small-M kernel,
+# see FEW_TILE_SHAPES): one K stage, fewer stages than the load ring, ragged
+# M and N, fewer tiles than CUs (grid not a multiple of 8), and more tiles
+# than CUs (several tiles per workgroup, the load ring running across tile
+# boundaries).
 LARGE_SHAPES = [
-    (256, 256, 128), (257, 300, 256), (520, 1030, 384), (96, 2048, 512),
-    (700, 100, 640), (1024, 768, 1024), (4352, 4352, 128), (2304, 4608, 384),
+    (2304, 512, 128), (1030, 2100, 256), (520, 1030, 384), (96, 2048, 512),
+    (2200, 100, 640), (1024, 768, 1024), (4352, 4352, 128), (2304, 4608, 384),
 ]
 
 
@@ -109,9 +111,26 @@ def test_large_tile_shapes(m, n, k):
     check_full(ac, as_, bc, bs, "large-tile")
 
 
+# Shapes with M > 64 and fewer than 8 output tiles of 256 x 256: the small-M
+# kernel with one grid row per 64 activation rows (tiny layers, where one
+# large tile per workgroup would leave the chip idle), both layouts, K tails.
+FEW_TILE_SHAPES = [(128, 128, 256), (256, 256, 128), (257, 300, 256), (700, 100, 640), (300, 500, 2048),
+                   (130, 260, 544), (65, 1792, 4096), (768, 512, 96)]
+
+
+@pytest.mark.parametrize("m,n,k", FEW_TILE_SHAPES)
+def test_few_tile_shapes(m, n, k):
+    rng = np.random.default_rng(m * 5 + n * 11 + k)
+    ac, as_ = workloads.random_mxfp4(rng, m, k)
+    bc, bs = workloads.random_mxfp4(rng, n, k)
+    check_full(ac, as_, bc, bs, "few tiles")
+    if k % 128 == 0:
+        test_tiled_operands(m, n, k)
+
+
 def test_large_tile_strided_output():
     rng = np.random.default_rng(80)
-    m, n, k = 300, 520, 256
+    m, n, k = 520, 2100, 256
     ac, as_ = workloads.random_mxfp4(rng, m, k)
     bc, bs = workloads.random_mxfp4(rng, n, k)
     for dt, fill in ((torch.float32, 7.0), (torch.bfloat16, 3.0)):
@@ -130,7 +149,7 @@ def test_large_tile_strided_output():
 
 TILED_SHAPES = [
     (256, 256, 128), (257, 300, 256), (1000, 520, 384), (16, 1000, 256), (96, 2048, 512),
-    (4352, 4352, 128), (2304, 4608, 384)]
+    (4352, 4352, 128), (2304, 4608, 384), (600, 2100, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", TILED_SHAPES)
@@ -202,7 +221,7 @@ def test_small_m_strided_output():
         assert (host[:, :off] == fill).all() and (host[:, off + n:] == fill).all()   # no stray writes
 
 
-@pytest.mark.parametrize("m,n,k", [(20, 300, 256), (40, 70, 384), (300, 520, 256)])
+@pytest.mark.parametrize("m,n,k", [(20, 300, 256), (40, 70, 384), (300, 520, 256), (600, 2100, 256)])
 def test_tiled_padding_is_ignored(m, n, k):
     """Padding rows of tiled operands hold garbage (code bytes 0xFF = -6, scale
     bytes 0xFF = NaN): no stored output may depend on them (small-M and

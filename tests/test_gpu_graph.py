@@ -32,7 +32,7 @@ def kron_rot(seed=3):
 
 
 @pytest.mark.parametrize("rot", [None, "h32", "kron"])
-@pytest.mark.parametrize("m,n,k", [(300, 520, 512), (16, 384, 1024)])
+@pytest.mark.parametrize("m,n,k", [(300, 520, 512), (16, 384, 1024), (600, 2100, 512)])
 def test_captured_step_matches_eager(m, n, k, rot):
     rng = np.random.default_rng(m + n + k)
     r = kron_rot() if rot == "kron" else rot
