@@ -131,6 +131,36 @@ __device__ __forceinline__ uint32_t encode_block(const float (&v)[32], uint32_t 
   return sbyte;
 }
 
+// Block amax, E8M0 byte and codes of an untransformed bf16 block, straight
+// from its 16 packed dwords (element 2j in the low half of dword j).  For
+// finite bf16 values the magnitude bits order like the magnitudes, so the
+// block amax is a packed 16-bit unsigned max over the bits with the sign
+// cleared, and its biased exponent is those bits >> 7 -- the fp32 exponent
+// field of the same value.  The converter then reads the bf16 pairs directly
+// (widening bf16 to fp32 is exact, so this is the f32 conversion of the
+// widened values).  Same bytes as widening, encode_block and the f32
+// converter, with neither the widening nor a float max per element.
+__device__ __forceinline__ uint32_t encode_block_bf16(const uint32_t (&d)[16], uint32_t (&w)[4]) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, d[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, d[i] & 0x7FFF7FFFu));
+  const uint32_t ef = (uint32_t)(m[0] > m[1] ? m[0] : m[1]) >> 7;
+  const uint32_t sbyte = ef > 2u ? ef - 2u : 0u;
+  const float scale = scale_of(sbyte);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t acc = 0;
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(acc, __builtin_bit_cast(bf16x2, d[4 * i + 0]), scale, 0);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(acc, __builtin_bit_cast(bf16x2, d[4 * i + 1]), scale, 1);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(acc, __builtin_bit_cast(bf16x2, d[4 * i + 2]), scale, 2);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(acc, __builtin_bit_cast(bf16x2, d[4 * i + 3]), scale, 3);
+    w[i] = acc;
+  }
+  return sbyte;
+}
+
 // Value of a 4-bit E2M1 code (bit 3 the sign).
 __device__ __forceinline__ double e2m1_value(uint32_t c) {
   const uint32_t m = c & 7u;

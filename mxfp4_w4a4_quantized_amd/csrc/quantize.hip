@@ -164,28 +164,38 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int den
 #pragma unroll
   for (int q = 0; q < CPB; ++q) q4[q] = slab[wave][lane * CPB + (q ^ slab_swz<CPB>(lane))];
 
-  float v[32];
-  if constexpr (BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = bf16_lo(q4[i][j]);
-        v[8 * i + 2 * j + 1] = bf16_hi(q4[i][j]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[4 * i + j] = __uint_as_float(q4[i][j]);
-  }
-
-  // smoothing factors of this block's 32 channels (block column within its row)
-  const uint32_t kcol = (!a.tiled && dense) ? ocol % a.nblk_row : ocol;
-  rotate_block<ROT, P, Q>(ROT == 3 ? a.fa + 32 * kcol : a.fa, a.fb, v);
   uint32_t w[4];
-  const uint32_t sbyte = encode_block_sel<FIT>(v, w);
+  uint32_t sbyte;
+  if constexpr (BF16 && ROT == 0 && !FIT) {
+    // no transform: amax and codes straight from the packed bf16 pairs
+    uint32_t d[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[4 * i + j] = q4[i][j];
+    sbyte = encode_block_bf16(d, w);
+  } else {
+    float v[32];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = bf16_lo(q4[i][j]);
+          v[8 * i + 2 * j + 1] = bf16_hi(q4[i][j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * i + j] = __uint_as_float(q4[i][j]);
+    }
+    // smoothing factors of this block's 32 channels (block column within its row)
+    const uint32_t kcol = (!a.tiled && dense) ? ocol % a.nblk_row : ocol;
+    rotate_block<ROT, P, Q>(ROT == 3 ? a.fa + 32 * kcol : a.fa, a.fb, v);
+    sbyte = encode_block_sel<FIT>(v, w);
+  }
   if (a.tiled) {
     const uint32_t t = orow / kTileRows, r = orow % kTileRows, sg = ocol / 4, cb = ocol % 4;
     const uint64_t ts = (uint64_t)t * nstage + sg;   // (tile, stage) index

@@ -25,6 +25,7 @@ import torch
 
 import mxfp4_w4a4_quantized_amd as mx
 import oracle
+import workloads
 
 pytestmark = pytest.mark.gpu
 
@@ -83,3 +84,37 @@ def test_converter_every_scale_byte():
         assert np.array_equal(gc, rc), f"scale byte {s}: {np.count_nonzero(gc != rc)} code bytes differ"
         if s % 32 == 0 or s == 252:
             print(f"[progress] scale byte {s} ok ({nb} blocks)", flush=True)
+
+
+def test_bf16_converter_every_scale_byte():
+    """bf16 activations (the quantizer converts their packed pairs directly
+    when there is no transform): every bf16 value t in [0, 8), both signs,
+    scaled by 2^e and rounded to bf16 on the host, at every reachable scale
+    byte, in both output layouts and through the Hadamard path (which widens
+    to fp32 first); codes and scales equal the oracle's on the same bf16
+    inputs."""
+    t = workloads.bf16_to_f32(np.arange(0, 0x4100, dtype=np.uint16))          # every bf16 in [0, 8)
+    vals = np.concatenate([t, -t]).astype(np.float32)
+    print(f"[case] bf16 converter sweep: {vals.size} values per scale byte, bytes 0..252", flush=True)
+    for s in range(0, 253):
+        e = s - 127
+        x32, nb = blocks_at(vals, e)
+        xb = workloads.bf16_bits(x32)                     # t * 2^e rounded to bf16 (exact above the subnormals)
+        assert np.array_equal(workloads.bf16_to_f32(xb.reshape(-1)[::32][:nb]), x32.reshape(-1)[::32][:nb])
+        xd = torch.from_numpy(xb.view(np.int16)).to(DEV).view(torch.bfloat16)
+        rc, rs = oracle.quantize(xb, bf16=True)
+        assert (rs.reshape(-1)[:nb] == s).all()
+        for layout in (mx.ROWMAJOR, mx.TILED):
+            c, sc = mx.quantize_rotate(xd, layout=layout)
+            torch.cuda.synchronize()
+            gc, gs = c.cpu().numpy(), sc.cpu().numpy()
+            if layout == mx.TILED:
+                gc, gs = mx.untile_host(gc, gs, xb.shape[0])
+            assert np.array_equal(gs, rs), f"scale byte {s}: {np.count_nonzero(gs != rs)} scale bytes differ"
+            assert np.array_equal(gc, rc), f"scale byte {s}: {np.count_nonzero(gc != rc)} code bytes differ"
+        if s % 32 == 0:
+            hc, hs = mx.quantize_rotate(xd, mx.HADAMARD32)
+            torch.cuda.synchronize()
+            rhc, rhs = oracle.quantize(xb, rot="h32", bf16=True)
+            assert np.array_equal(hc.cpu().numpy(), rhc) and np.array_equal(hs.cpu().numpy(), rhs)
+            print(f"[progress] bf16 scale byte {s} ok ({nb} blocks)", flush=True)
