@@ -86,10 +86,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // STRIDED: load i of wave w takes KiB i * waves + w, so every load
 // instruction of the grid sweeps the buffer in step (the decode GEMM's waves
 // read one KiB from each of several 16 KiB stage blocks); else the wave's
-// rk KiB are contiguous (the quantizer's waves).
-template <int RK, bool STRIDED>
+// rk KiB are contiguous (the quantizer's waves).  The store count is a
+// template parameter so the loaded registers are indexed at compile time.
+template <int RK, int WK, bool STRIDED>
 __global__ __launch_bounds__(256) void stream_loop(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                    int64_t waves, int wk) {
+                                                    int64_t waves) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wave >= waves) return;
@@ -97,14 +98,16 @@ __global__ __launch_bounds__(256) void stream_loop(const u32x4* __restrict__ src
 #pragma unroll
   for (int i = 0; i < RK; ++i)
     v[i] = __builtin_nontemporal_load(src + (STRIDED ? (i * waves + wave) : (wave * RK + i)) * 64 + lane);
-  u32x4* d = dst + wave * wk * 64 + lane;
-  for (int i = 0; i < wk; ++i) {   // each store carries data of every load
+  u32x4* d = dst + wave * WK * 64 + lane;
+#pragma unroll
+  for (int i = 0; i < WK; ++i) {   // each store carries data of every load
     u32x4 x = v[i];
 #pragma unroll
-    for (int j = 0; j < RK; ++j) x ^= j == i ? u32x4{0u, 0u, 0u, 0u} : v[j];
+    for (int j = 0; j < RK; ++j)
+      if (j != i) x ^= v[j];
     __builtin_nontemporal_store(x, d + 64 * i);
   }
-  if (wk == 0) {   // keep the loads live: a store that never happens in practice
+  if constexpr (WK == 0) {   // keep the loads live: a store that never happens in practice
     u32x4 x = v[0];
 #pragma unroll
     for (int j = 1; j < RK; ++j) x ^= v[j];
@@ -116,8 +119,8 @@ __global__ __launch_bounds__(256) void stream_loop(const u32x4* __restrict__ src
 
 // waves waves of 64 lanes (4 per workgroup); wave w reads rk KiB of src (KiB
 // rk w .. rk w + rk - 1 for rk = 4 or 8, KiB i waves + w for i < 16 when rk =
-// 16) and writes KiB wk w .. wk w + wk - 1 of dst (0 <= wk <= rk; dst at
-// least 1 KiB when wk == 0).  src holds waves * rk
+// 16) and writes KiB wk w .. wk w + wk - 1 of dst ((rk, wk) one of (4, 0),
+// (4, 1), (8, 0), (8, 2), (16, 0); dst at least 1 KiB when wk == 0).  src holds waves * rk
 // KiB, dst waves * max(wk, 1) KiB, both 16-byte aligned device memory.
 // Returns 0, or a HIP error code.
 extern "C" __attribute__((visibility("default"))) int mxfp4_ceiling_stream(const void* src, void* dst, long long waves,
@@ -129,12 +132,12 @@ extern "C" __attribute__((visibility("default"))) int mxfp4_ceiling_stream(const
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const u32x4* a = static_cast<const u32x4*>(src);
   u32x4* b = static_cast<u32x4*>(dst);
-  switch (rk) {
-    case 4: stream_loop<4, false><<<grid, block, 0, s>>>(a, b, waves, wk); break;
-    case 8: stream_loop<8, false><<<grid, block, 0, s>>>(a, b, waves, wk); break;
-    case 16: stream_loop<16, true><<<grid, block, 0, s>>>(a, b, waves, wk); break;
-    default: return (int)hipErrorInvalidValue;
-  }
+  if (rk == 4 && wk == 0) stream_loop<4, 0, false><<<grid, block, 0, s>>>(a, b, waves);
+  else if (rk == 4 && wk == 1) stream_loop<4, 1, false><<<grid, block, 0, s>>>(a, b, waves);
+  else if (rk == 8 && wk == 0) stream_loop<8, 0, false><<<grid, block, 0, s>>>(a, b, waves);
+  else if (rk == 8 && wk == 2) stream_loop<8, 2, false><<<grid, block, 0, s>>>(a, b, waves);
+  else if (rk == 16 && wk == 0) stream_loop<16, 0, true><<<grid, block, 0, s>>>(a, b, waves);
+  else return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 
