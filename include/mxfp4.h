@@ -221,15 +221,17 @@ MXFP4_API mxfp4_status mxfp4_gemm_requant(const uint8_t* a_codes, const uint8_t*
                                           int64_t k, int32_t layout, uint8_t* y_codes, uint8_t* y_scales,
                                           int32_t y_layout, void* stream);
 
-/* Fused small-M linear layer Y = Q(rot(X)) * W^T for decode shapes: the
- * activations are rotated and quantized inside the GEMM kernel, straight into
- * the matrix-core operands, so the quantized activations never reach memory
- * and the layer is one launch.  The rotation "fused into the quantization and
- * matmul kernels" is the design of "Bridging the Gap Between Promise and
- * Performance for Microscaling FP4 Quantization", "GPU Kernel Ondersteuning
- * (QuTLASS)".  The quantized activations equal mxfp4_quantize_rotate's bit
- * for bit; Y agrees with mxfp4_quantize_rotate followed by mxfp4_gemm within
- * the GEMM's fp32 rounding (the K sums are taken in another order).
+/* Fused small-M linear layer Y = Q(rot(X)) * W^T for decode shapes, in one
+ * kernel launch: the activations are rotated and quantized inside the GEMM
+ * kernel, and the weights start streaming from HBM while that happens.  The
+ * rotation "fused into the quantization and matmul kernels" is the design of
+ * "Bridging the Gap Between Promise and Performance for Microscaling FP4
+ * Quantization", "GPU Kernel Ondersteuning (QuTLASS)".  A few workgroups
+ * quantize X into the workspace (1152 bytes per 16 rows and 128 columns, in
+ * the matrix cores' operand order) and the others wait for them on a
+ * device-scope counter.  The quantized activations equal
+ * mxfp4_quantize_rotate's bit for bit, and Y equals mxfp4_quantize_rotate
+ * followed by mxfp4_gemm bit for bit (the same K split and summation order).
  *   x       device, [m][ld_x] BF16 activations, 16-byte aligned, ld_x a
  *           multiple of 8, ld_x >= k.
  *   rot     NULL / NONE, HADAMARD32, SMOOTH, or KRON with 2 <= p <= 16.
@@ -237,20 +239,23 @@ MXFP4_API mxfp4_status mxfp4_gemm_requant(const uint8_t* a_codes, const uint8_t*
  *   m       1 <= m <= 64 (0 is a no-op); n >= 0; k > 0 multiple of 32 (of
  *           128 for TILED).
  *   y       device, [m][ld_y] of y_dtype (F32 or BF16), ld_y >= n.
- *   workspace, workspace_bytes  device scratch for the split over K, of at
- *           least mxfp4_linear_small_workspace(m, n, k) bytes, 256-byte
- *           aligned (NULL and 0 when that size is 0, i.e. k <= 1024).  Its
- *           first 64 KiB are counters of the groups of 256 weight rows, the
- *           same region for every shape; they must be zero before the
- *           workspace's first use (e.g. one hipMemset), and every call leaves
- *           them zero when its kernel completes, so one workspace serves
- *           calls of any shape in stream order.  Calls that may run at the
- *           same time (other streams, other host threads) need workspaces of
- *           their own.
+ *   workspace, workspace_bytes  device scratch of at least
+ *           mxfp4_linear_small_workspace(m, n, k) bytes, 256-byte aligned.
+ *           Its first 4 KiB hold the handoff counters, the same region for
+ *           every shape.  They must be zero before the workspace's first use
+ *           (e.g. one hipMemset), and every call leaves them zero when its
+ *           kernel completes, so one workspace serves calls of any shape in
+ *           stream order.  The 32-bit word at byte 2048 of that region is
+ *           set to a nonzero value if a workgroup ever stopped waiting for
+ *           the quantized activations at its bound (2^20 polls, tens of
+ *           milliseconds; then that call's Y is undefined); no call clears
+ *           it.  Calls that may run at the same time (other streams, other
+ *           host threads) need workspaces of their own.
  * Errors: INVALID_ARG as for mxfp4_quantize_rotate and mxfp4_gemm, and for a
  *   missing or short workspace; UNSUPPORTED for m > 64, F32 activations, a
- *   KRON rotation with p = 1 or p = 32, or misaligned pointers (use
- *   mxfp4_quantize_rotate + mxfp4_gemm there); HIP if the launch fails. */
+ *   KRON rotation with p = 1 or p = 32, misaligned pointers (use
+ *   mxfp4_quantize_rotate + mxfp4_gemm there), or a workspace image of
+ *   2 GiB or more; HIP if the launch fails. */
 MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_t m, int64_t k,
                                           int64_t ld_x, const mxfp4_rotation* rot,
                                           const uint8_t* w_codes, const uint8_t* w_scales, int64_t n,
@@ -260,14 +265,14 @@ MXFP4_API mxfp4_status mxfp4_linear_small(const void* x, int32_t x_dtype, int64_
 /* mxfp4_linear_small for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments and result as mxfp4_linear_small without the
- * workspace: the split over K uses a fixed 16 MiB array of device memory
- * inside the library instead (one per GPU, held until the process ends; its
+ * workspace: the workspace is a fixed 4 MiB array of device memory inside
+ * the library instead (one per GPU, held until the process ends; its
  * counters are cleared by the first call on each device).  The call
  * allocates nothing.  Every call on a GPU shares that GPU's array, so calls
  * that overlap in time on one GPU (other streams, other host threads) race:
  * serialize them, or give each its own workspace with mxfp4_linear_small.
- * Limit: mxfp4_linear_small_workspace(m, n, k) <= 16 MiB (for m = 16 and
- * k = 4096, n <= 65280).
+ * Limit: mxfp4_linear_small_workspace(m, n, k) <= 4 MiB (k <= 465536 for
+ * m <= 16, k <= 116352 for m <= 64).
  * Errors: as mxfp4_linear_small, and UNSUPPORTED past that limit (checked
  *   before anything is launched); HIP if the scratch address lookup or a
  *   launch fails. */
@@ -277,14 +282,13 @@ MXFP4_API mxfp4_status mxfp4_linear_small_noalloc(const void* x, int32_t x_dtype
                                                   int32_t layout, void* y, int32_t y_dtype, int64_t ld_y,
                                                   void* stream);
 
-/* Workspace size of mxfp4_linear_small for (m, n, k): 0 when k <= 1024 (one
- * K slice), else 64 KiB of group counters plus ceil(k / 1024) fp32 partial
- * tiles of m x 256 ceil(n / 256).  The fused layer over 16 x 4096 -> 14336
- * needs 3.74 MB.
+/* Workspace size of mxfp4_linear_small for (m, n, k): 0 when m or n is 0,
+ * else 4 KiB of counters plus 1152 ceil(m / 16) ceil(k / 128) bytes for the
+ * quantized activations (40 960 bytes for 16 x 4096 -> 14336).
  * Errors: INVALID_ARG for a null pointer, negative sizes, k not a positive
- *   multiple of 32; UNSUPPORTED for m > 64, k >= 2^30, and, when k > 1024,
- *   n > 4194304 (16384 counters) or partial tiles of 2 GiB or more
- *   (mxfp4_linear_small returns UNSUPPORTED for the same shapes). */
+ *   multiple of 32; UNSUPPORTED for m > 64, n or k >= 2^30, or an
+ *   activation image of 2 GiB or more (mxfp4_linear_small returns
+ *   UNSUPPORTED for the same shapes). */
 MXFP4_API mxfp4_status mxfp4_linear_small_workspace(int64_t m, int64_t n, int64_t k, int64_t* bytes);
 
 /* Buffer sizes of a TILED operand with `rows` rows and `k` columns (k > 0, a
@@ -322,7 +326,7 @@ MXFP4_API mxfp4_status mxfp4_smooth_weight_factors(const float* r, int64_t k, fl
 MXFP4_API const char* mxfp4_status_string(int32_t status);
 
 /* ABI version of this header (bumped on incompatible changes). */
-#define MXFP4_ABI_VERSION 3
+#define MXFP4_ABI_VERSION 4
 MXFP4_API int32_t mxfp4_abi_version(void);
 
 #ifdef __cplusplus

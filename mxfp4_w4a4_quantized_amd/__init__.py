@@ -329,8 +329,8 @@ def linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, rot=N
 
 
 def linear_small_workspace_bytes(m: int, n: int, k: int) -> int:
-    """Device workspace that mxfp4_linear_small needs for (m, n, k) (0 when K
-    fits one slice of 1024)."""
+    """Device workspace that mxfp4_linear_small needs for (m, n, k): 4 KiB of
+    counters plus the quantized activations (0 when m or n is 0)."""
     b = ctypes.c_int64()
     _check(lib().mxfp4_linear_small_workspace(m, n, k, ctypes.byref(b)), "mxfp4_linear_small_workspace")
     return b.value
@@ -355,10 +355,10 @@ def linear_small(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
                  out_dtype=torch.bfloat16, y: torch.Tensor = None, layout: int = ROWMAJOR,
                  n: int = None, workspace: torch.Tensor = None) -> torch.Tensor:
     """Fused small-M linear layer (decode): bf16 x [m, k] with 1 <= m <= 64 is
-    rotated and quantized inside the GEMM (one launch, no quantized
-    activations in memory); same result as linear() within the GEMM's fp32
-    rounding.  `workspace` (uint8, zero-filled before its first use) defaults
-    to one kept per device and stream."""
+    rotated and quantized inside the GEMM kernel (one launch; the quantized
+    activations pass through `workspace`); the same bytes as linear() with
+    the same layout.  `workspace` (uint8, zero-filled before its first use)
+    defaults to one kept per device and stream."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     m, k = x.shape
@@ -395,10 +395,10 @@ def linear_small(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
 
 def linear_small_noalloc(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, y: torch.Tensor,
                          rot=None, layout: int = ROWMAJOR) -> torch.Tensor:
-    """linear_small for callers that cannot allocate: the split over K uses
-    the library's fixed 16 MiB per-GPU scratch (mxfp4_linear_small_noalloc);
-    y [m, n] is the caller's.  Calls that overlap in time on one GPU share
-    that scratch and race."""
+    """linear_small for callers that cannot allocate: the workspace is the
+    library's fixed 4 MiB per-GPU scratch (mxfp4_linear_small_noalloc); y
+    [m, n] is the caller's.  Calls that overlap in time on one GPU share that
+    scratch and race."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     m, k = x.shape

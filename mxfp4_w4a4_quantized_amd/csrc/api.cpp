@@ -206,9 +206,9 @@ MXFP4_API mxfp4_status mxfp4_linear_small_workspace(int64_t m, int64_t n, int64_
   if (bytes == nullptr || m < 0 || n < 0 || k <= 0 || (k % 32) != 0) return MXFP4_ERR_INVALID_ARG;
   if (m > 64) return MXFP4_ERR_UNSUPPORTED;
   if (n >= kMaxDim || k >= kMaxDim) return MXFP4_ERR_UNSUPPORTED;
-  const int64_t need = (m == 0 || n == 0) ? 0 : mxfp4::linear_small_workspace_bytes(m, n, k);
-  if (need > 0 && (n > mxfp4::kLinearMaxN || need - mxfp4::kLinearCounterBytes >= (int64_t(1) << 31)))
-    return MXFP4_ERR_UNSUPPORTED;
+  const int64_t need = (m == 0 || n == 0) ? 0 : mxfp4::linear_small_workspace_bytes(m, k);
+  // the quantized activations are addressed with 32-bit byte offsets
+  if (need - mxfp4::kLinearCounterBytes >= (int64_t(1) << 31)) return MXFP4_ERR_UNSUPPORTED;
   *bytes = need;
   return MXFP4_OK;
 }
@@ -241,10 +241,9 @@ mxfp4_status linear_small_impl(const void* x, int32_t x_dtype, int64_t m, int64_
   if (tiled && !aligned(w_scales, 4)) return MXFP4_ERR_UNSUPPORTED;
   const int64_t ybytes = (y_dtype == MXFP4_BF16) ? 2 : 4;
   if (!aligned(y, ybytes)) return MXFP4_ERR_UNSUPPORTED;
-  const int64_t need = mxfp4::linear_small_workspace_bytes(m, n, k);
-  // the partial tiles are addressed with 32-bit byte offsets
-  if (need > 0 && (n > mxfp4::kLinearMaxN || need - mxfp4::kLinearCounterBytes >= (int64_t(1) << 31)))
-    return MXFP4_ERR_UNSUPPORTED;
+  const int64_t need = mxfp4::linear_small_workspace_bytes(m, k);
+  // the quantized activations are addressed with 32-bit byte offsets
+  if (need - mxfp4::kLinearCounterBytes >= (int64_t(1) << 31)) return MXFP4_ERR_UNSUPPORTED;
   if (use_static && need > mxfp4::kLinearStaticScratchBytes) return MXFP4_ERR_UNSUPPORTED;
 
   mxfp4::LinearArgs L;
@@ -267,19 +266,16 @@ mxfp4_status linear_small_impl(const void* x, int32_t x_dtype, int64_t m, int64_
   L.g.ld_y = ld_y;
   L.g.y_bf16 = (y_dtype == MXFP4_BF16);
   L.g.tiled = tiled;
-  if (need > 0) {
-    if (use_static) {
-      const hipError_t e = mxfp4::linear_small_static_scratch(&workspace, static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) return MXFP4_ERR_HIP;
-      workspace_bytes = mxfp4::kLinearStaticScratchBytes;
-    }
-    if (workspace == nullptr || workspace_bytes < need) return MXFP4_ERR_INVALID_ARG;
-    if (!aligned(workspace, 256)) return MXFP4_ERR_UNSUPPORTED;
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    L.counters = reinterpret_cast<uint32_t*>(ws);
-    L.partials = reinterpret_cast<float*>(ws + mxfp4::kLinearCounterBytes);
-    L.ld_part = (n + 255) / 256 * 256;
+  if (use_static) {
+    const hipError_t e = mxfp4::linear_small_static_scratch(&workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return MXFP4_ERR_HIP;
+    workspace_bytes = mxfp4::kLinearStaticScratchBytes;
   }
+  if (workspace == nullptr || workspace_bytes < need) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return MXFP4_ERR_UNSUPPORTED;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  L.counters = reinterpret_cast<uint32_t*>(ws);
+  L.xq = ws + mxfp4::kLinearCounterBytes;
   return from_hip(mxfp4::launch_linear_small(L, static_cast<hipStream_t>(stream)));
 }
 

@@ -527,6 +527,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+}  // namespace
+
 // CU count of the current device, cached per device.  Calls may come from
 // several host threads at once: the cache slots are atomics (every writer
 // stores the same value).
@@ -541,8 +543,6 @@ int cu_count() {
   }
   return n;
 }
-
-}  // namespace
 
 bool gemm_large_supported(const GemmArgs& g) {
   const int64_t m = (g.m + BM - 1) / BM * BM, n = (g.n + BN - 1) / BN * BN;   // padded rows

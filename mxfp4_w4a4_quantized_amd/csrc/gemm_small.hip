@@ -368,36 +368,65 @@ void launch_mg(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s)
 
 
 // ---------------------------------------------------------------------------
-// Fused small-M linear layer: Y = Q(rot(X)) * W^T with the activation
-// quantization done inside the GEMM, one launch, no quantized activations in
-// memory (the rotation fused into the quantization and the matmul, as in
-// "Bridging the Gap Between Promise and Performance for Microscaling FP4
-// Quantization", "GPU Kernel Ondersteuning (QuTLASS)").
+// Fused small-M linear layer: Y = Q(rot(X)) * W^T in one launch, with the
+// activation rotation and quantization done inside the GEMM kernel (the
+// rotation fused into the quantization and the matmul, as in "Bridging the
+// Gap Between Promise and Performance for Microscaling FP4 Quantization",
+// "GPU Kernel Ondersteuning (QuTLASS)").
 //
-// Split over K.  Workgroup (grp, slice) takes LNR = 256 weight rows and a
-// slice of LKS = 8 K steps (1024 elements).  It first rotates and quantizes
-// the part of X that slice needs -- 16 MG rows x 32 blocks, one block per
-// thread and M group, with the quantizer's own arithmetic (block_quant.h, so
-// the codes equal the quantizer's bit for bit) -- into LDS, already in the
-// MFMA operand order.  Every block of X is then quantized by N / 256
-// workgroups instead of by every workgroup of a full-K split: for a Kronecker
-// transform (384 FMAs per block) that is what lets the arithmetic hide under
-// the weight stream.  The activation loads are issued before the weight
-// loads (vector memory completes in order) so the quantization runs while
-// the weights stream in.  The 8 waves then take 32 weight rows each over the
-// slice's steps, reading the quantized activations from LDS.
+// The compute waves are those of gemm_small_kernel: K split over the waves
+// in chunks of CH steps (the same split), the same MFMA chains and the same
+// LDS reduction, so Y equals mxfp4_quantize_rotate followed by mxfp4_gemm
+// bit for bit.  A workgroup takes 16 NG weight rows and has one more wave,
+// its sync wave:
+//  * The sync waves of the first `nprod` workgroups rotate and quantize X.
+//    A pass takes one unit of 16 rows x 128 elements (one K step of one M
+//    group), one block per lane, with the quantizer's own arithmetic
+//    (block_quant.h).  The codes and scales go into the workspace already in
+//    MFMA operand order, through device-coherent (sc1) stores that write
+//    through the XCD's L2.  The wave waits for its stores, then counts its
+//    workgroup on a device-scope counter, kept in 16 copies on separate
+//    lines.
+//  * Every sync wave polls one copy of that counter until all producers have
+//    counted, then releases its workgroup's compute waves at a barrier.
+//    (With one copy, the increments queued behind a couple of hundred
+//    pollers of the same address: 2.4 us from the last increment to the
+//    polls seeing it.)
+//  * The compute waves issue their first chunk of weight loads before that
+//    barrier, so the weight stream (the layer's HBM-bound part) runs while X
+//    is quantized and handed over.  After the barrier they read the
+//    quantized X with device-coherent loads, which cannot hit a stale L2 copy
+//    from an earlier call, and run the MFMAs as the weights arrive.
+// The compute waves never poll themselves.  A wave's vector loads complete
+// in order, so a poll issued behind a weight chunk would wait for all of it.
+// A workgroup that waits holds its CU, and a workgroup of 5 or 9 waves takes
+// a CU's wave slots (one per SIMD per 4 waves, rounded up, at the register
+// budget of these kernels).  So up to 4 compute waves and 16 activation rows
+// take 64 weight rows per workgroup (224 workgroups for 14336 rows, all
+// resident at once); a grid larger than the CU count still completes, the
+// later workgroups starting as the first ones finish, but takes about a
+// second round.
 //
-// With one slice the workgroup stores Y.  With S > 1 slices every workgroup
-// stores its fp32 partial tile into the workspace and counts itself on a
-// device-scope counter of its 256-row group; the last one to finish sums the
-// S partials in slice order (so Y does not depend on which workgroup
-// finishes last), stores Y, and sets the counter back to zero: the counters
-// are zero again whenever the kernel has completed.  The workspace holds
-// 4 S m * 256 ceil(n / 256) bytes of partials (the partial tiles' byte
-// offsets are 32-bit: below 2 GiB).
-constexpr int LNR = 256;      // weight rows per workgroup
-constexpr int LKS = 8;        // K steps per slice
-constexpr int LWAVES = 8;     // waves per workgroup, 32 weight rows each
+// Termination.  Producers wait on nothing before they count, and they are
+// the lowest-numbered workgroups, which the dispatcher places first.  The
+// poll is bounded all the same (2^20 polls, tens of milliseconds); past the
+// bound the sync wave sets an error word in the workspace and goes on, and
+// that call's Y is undefined.
+//
+// Reset.  Once its compute waves are released, each sync wave counts itself
+// on the counter of its group of workgroups; the last of a group clears that
+// counter and counts the group on a top counter, and the last group clears
+// the top counter and the producer counts.  So every counter is zero
+// whenever the kernel has completed, and calls in stream order can share one
+// workspace.  (One counter for the whole grid serialized several hundred
+// atomics on one address: about 2 us.)
+constexpr int LPROD_MAX = 64;                // producer workgroups at most (8 per XCD)
+constexpr uint32_t LPOLL_LIMIT = 1u << 20;   // polls before a sync wave gives up
+constexpr int LLINE = 32;                    // counter words 128 bytes apart
+constexpr int LREPL = 16;                    // copies of the producer count, one line each
+constexpr int CNT_PRODUCED = 0, CNT_ERROR = LREPL * LLINE, CNT_TOP = CNT_ERROR + LLINE, CNT_GROUP0 = CNT_TOP + LLINE;
+constexpr int LGROUPS_MAX = (int)(kLinearCounterBytes / 4 / LLINE) - LREPL - 2;
+constexpr int kCoherent = 16;                // buffer cache policy sc1: device scope
 
 template <bool XBF16>
 struct RawBlock {
@@ -435,206 +464,280 @@ __device__ __forceinline__ void quantize_raw(const RawBlock<XBF16>& b, const flo
   codes = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int MG, int ROT, int P, int Q, bool TILED>
-__global__ __launch_bounds__(64 * LWAVES) void linear_small_kernel(LinearArgs L, int nslices, int y_vec) {
-  __shared__ u32x4 xq[MG][LKS][64];       // quantized activations, MFMA operand order
-  __shared__ uint8_t xsc[MG][LKS][64];    // their scale bytes
-  __shared__ int last_flag;
-  const GemmArgs& g = L.g;
+// Workspace image of the quantized activations: unit u = mg * nsteps + s
+// (M group mg, K step s) holds 64 lanes x 16 code bytes at 1024 u -- lane l
+// the block l / 16 of row l % 16, as the MFMA reads it -- and, at
+// 1024 units + 128 u, the scale bytes as 16 dwords, dword r holding the
+// step's four block scales of row r (the layout scales_dw reads).
+__device__ __forceinline__ uint32_t xq_code_off(int u, int lane) { return ((uint32_t)u * 64u + lane) * 16u; }
+__device__ __forceinline__ uint32_t xq_scale_off(int units, int u, int row) {
+  return (uint32_t)units * 1024u + (uint32_t)u * 128u + 4u * row;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Sync wave of a producer workgroup: quantize its units of X into the
+// workspace, then count the workgroup once its stores have completed.
+template <int ROT, int P, int Q>
+__device__ __forceinline__ void produce(const LinearArgs& L, const __amdgpu_buffer_rsrc_t& xr, int units, int nsteps,
+                                        int kblocks, int nprod, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
-  const int grp = blockIdx.x, slice = blockIdx.y;
-  const int n0 = grp * LNR;
-  const int kblocks = g.k >> 5;
-  const int nsteps = (g.k + 127) >> 7;
-  const int s0 = slice * LKS;
-  const int s_end = min(nsteps, s0 + LKS);
   const uint8_t* xb = static_cast<const uint8_t*>(L.x);
-
-  // 1. the raw activation blocks this thread quantizes: block b = tid + 512 i
-  //    of the slice's [16 MG rows] x [32 block columns]
-  RawBlock<true> raw[MG];
-#pragma unroll
-  for (int i = 0; i < MG; ++i) {
-    const int b = tid + 64 * LWAVES * i;
-    const int row = b >> 5, col = 4 * s0 + (b & 31);
-    const bool ok = row < g.m && col < kblocks;
-    load_block<true>(xb + ((int64_t)(ok ? row : 0) * L.ld_x + (int64_t)(ok ? col : 0) * 32) * 2, ok, raw[i]);
-  }
-
-  // 2. this wave's weights: rows n0 + 32 wave + 16 f + lr over the slice's
-  //    steps, scales before codes.  Vector memory completes in order, so the
-  //    quantization below waits for the activation loads only and the scale
-  //    permutes for the scale loads only, while the code loads stream on.
-  //    Every lane issues the same loads whatever the shape: steps past the
-  //    slice or past K load from the slice's first step (always inside W) and
-  //    are zeroed afterwards, so the compiler's wait counts stay exact.
-  Operand w[2];
-#pragma unroll
-  for (int f = 0; f < 2; ++f)
-    w[f] = operand<TILED>(g.b_codes, g.b_scales, n0 + 32 * wave + 16 * f + lr, g.n, g.k, lg);
-  bool live[LKS];   // step s0 + j holds this lane's block
-#pragma unroll
-  for (int j = 0; j < LKS; ++j) live[j] = s0 + j < s_end && (TILED || 4 * (s0 + j) + lg < kblocks);
-  u32x4 wf[2][LKS];
-  int ws[2][LKS];
-  int wdw[2][LKS / 4];   // tiled: scale dwords, spread by permutes below
-  if constexpr (TILED) {
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int i4 = 0; i4 < LKS / 4; ++i4) {
-        const int st = min(s0 + 4 * i4 + lg, nsteps - 1);
-        wdw[f][i4] = *reinterpret_cast<const int*>(w[f].scale_row + (int64_t)st * w[f].sstride);
-      }
-  } else {
-#pragma unroll
-    for (int j = 0; j < LKS; ++j)
-#pragma unroll
-      for (int f = 0; f < 2; ++f) ws[f][j] = w[f].scale[(live[j] ? s0 + j : 0) * w[f].sstride - (live[j] ? 0 : lg)];
-  }
-#pragma unroll
-  for (int j = 0; j < LKS; ++j)
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int64_t off = live[j] ? (s0 + j) * w[f].cstride : (TILED ? s0 * w[f].cstride : -16 * lg);
-      wf[f][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[f].code + off));
-    }
-  // keep every load above the quantization (the scheduler would sink them to
-  // their first use, after it)
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 3. rotate and quantize into LDS: block (row, c) of the slice is the
-  //    operand of lane (row % 16) + 16 (c % 4) at step c / 4, M group row / 16
-#pragma unroll
-  for (int i = 0; i < MG; ++i) {
-    const int b = tid + 64 * LWAVES * i;
-    const int row = b >> 5, c = b & 31;
-    const int col = min(4 * s0 + c, kblocks - 1);   // smoothing: this block's 32 factors
+  for (int u = blockIdx.x; u < units; u += nprod) {
+    const int mg = u / nsteps, s = u - mg * nsteps;
+    const int row = 16 * mg + lr, c = 4 * s + lg;
+    const bool ok = row < L.g.m && c < kblocks;
+    RawBlock<true> raw;
+    load_block<true>(xb + ((int64_t)(ok ? row : 0) * L.ld_x + (int64_t)(ok ? c : 0) * 32) * 2, ok, raw);
     u32x4 codes;
     int sb;
-    quantize_raw<true, ROT, P, Q>(raw[i], ROT == 3 ? L.fa + 32 * col : L.fa, L.fb, codes, sb);
-    xq[row >> 4][c >> 2][(row & 15) + 16 * (c & 3)] = codes;
-    xsc[row >> 4][c >> 2][(row & 15) + 16 * (c & 3)] = (uint8_t)sb;
+    quantize_raw<true, ROT, P, Q>(raw, ROT == 3 ? L.fa + 32 * min(c, kblocks - 1) : L.fa, L.fb, codes, sb);
+    if (!ok) {   // rows past M and blocks past K: zero codes, zero scale byte
+      codes = u32x4{0u, 0u, 0u, 0u};
+      sb = 0;
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(codes, xr, (int)xq_code_off(u, lane), 0, kCoherent);
+    int d = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d |= (__shfl(sb, lr + 16 * j) & 0xFF) << (8 * j);
+    if (lg == 0) __builtin_amdgcn_raw_buffer_store_b32(d, xr, (int)xq_scale_off(units, u, lr), 0, kCoherent);
   }
-  if constexpr (TILED) {
-    // the scale of step s0 + 4 i + j for this lane's block lg is byte lg of
-    // lane (lr, j)'s dword i (see scales_dw)
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int i4 = 0; i4 < LKS / 4; ++i4)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ws[f][4 * i4 + j] = __shfl(wdw[f][i4], 16 * j + lr) >> (8 * lg);
-  }
-#pragma unroll
-  for (int j = 0; j < LKS; ++j)
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-      if (!live[j]) {
-        wf[f][j] = u32x4{0u, 0u, 0u, 0u};
-        ws[f][j] = 0;
-      }
-  __syncthreads();
+  // the stores have reached the device-coherent level before the count,
+  // which goes to every copy (lane i counts copy i)
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+  if (lane < LREPL)
+    __hip_atomic_fetch_add(L.counters + CNT_PRODUCED + LLINE * lane, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-  // 4. MFMAs over the slice
-  v4f acc[2][MG];
+// WB: waves per workgroup the kernel is compiled for (compute waves + 1).
+template <int MG, int NG, int WB, int ROT, int P, int Q, bool TILED>
+__global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int nwaves, int spw, int nprod,
+                                                                 int gsize, int y_vec) {
+  static_assert(MG * NG <= 2 * MAXACC, "reduction buffer size");
+  static_assert(CH % 4 == 0, "dword scale loads cover 4 steps");
+  __shared__ v4f red[MAXW][MG * NG][64];
+  __shared__ uint32_t red_ready;   // compute waves whose partial tile is in red
+  const GemmArgs& g = L.g;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NG;
+  const int kblocks = g.k >> 5;
+  const int nsteps = (g.k + 127) >> 7;
+  const int units = MG * nsteps;
+  const bool compute = wave < nwaves;
+  if (threadIdx.x == 0) {
+    red_ready = 0u;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): in LDS before the barrier below
+  }
+  const int s_begin = wave * spw;
+  const int s_end = min(nsteps, s_begin + spw);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(L.xq, 0, units * 1152, 0x00020000);
+
+  Operand w[NG];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int q = 0; q < NG; ++q) w[q] = operand<TILED>(g.b_codes, g.b_scales, n0 + 16 * q + lr, g.n, g.k, lg);
+  v4f acc[NG][MG];
 #pragma unroll
-    for (int mg = 0; mg < MG; ++mg) acc[f][mg] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < NG; ++q)
 #pragma unroll
-  for (int j = 0; j < LKS; ++j)
-    if (s0 + j < s_end) {
+    for (int mg = 0; mg < MG; ++mg) acc[q][mg] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // One chunk of this wave's weights, as gemm_small_kernel loads it.  Tiled
+  // scales stay packed (wsd: the dwords scales_dw loads), each spread to its
+  // lanes right before its MFMA, which keeps 24 registers free for the
+  // weight codes in flight.
+  u32x4 wf[NG][CH];
+  int ws[NG][CH];
+  int wsd[NG][CH / 4];
+  auto load_weights = [&](int s0) {
+    if constexpr (TILED) {   // steps past the range (never used) read the last step's dword
+#pragma unroll
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int i = 0; i < CH / 4; ++i)
+          wsd[q][i] = *reinterpret_cast<const int*>(w[q].scale_row +
+                                                    (int64_t)min(s0 + 4 * i + lg, nsteps - 1) * w[q].sstride);
+    }
+    const bool full = s0 + CH <= s_end && (TILED || 4 * (s0 + CH) <= kblocks);
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          wf[q][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[q].code + (s0 + j) * w[q].cstride));
+          if constexpr (!TILED) ws[q][j] = w[q].scale[(s0 + j) * w[q].sstride];
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          const int s = s0 + j;
+          wf[q][j] = u32x4{0u, 0u, 0u, 0u};
+          ws[q][j] = 0;
+          if (s < s_end && (TILED || 4 * s + lg < kblocks)) {
+            wf[q][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w[q].code + s * w[q].cstride));
+            if constexpr (!TILED) ws[q][j] = w[q].scale[s * w[q].sstride];
+          }
+        }
+    }
+  };
+  // the scale byte of weight fragment q at step s0 + j (in the low 8 bits)
+  auto wscale = [&](int q, int j) -> int {
+    if constexpr (TILED) return __shfl(wsd[q][j >> 2], 16 * (j & 3) + lr) >> (8 * lg);
+    else return ws[q][j];
+  };
+
+  // The compute waves and the sync wave meet at one barrier, each on its own
+  // path (no register of one path is live on the other).  A bare barrier: a
+  // workgroup fence would wait for the weight loads in flight.
+  if (compute) {
+    if (s_begin < s_end) load_weights(s_begin);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");   // keeps the activation loads below the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    for (int s0 = s_begin; s0 < s_end; s0 += CH) {
+      if (s0 != s_begin) load_weights(s0);
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg) {
-        const u32x4 xf = xq[mg][j][lane];
-        const int xs = xsc[mg][j][lane];
+        u32x4 xf[CH];
 #pragma unroll
-        for (int f = 0; f < 2; ++f) acc[f][mg] = mma(wf[f][j], xf, acc[f][mg], ws[f][j], xs);
+        for (int j = 0; j < CH; ++j) {
+          const int st = min(s0 + j, nsteps - 1);   // steps past the range are not used
+          xf[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xq_code_off(mg * nsteps + st, lane), 0, kCoherent);
+        }
+        int xsd[CH / 4];
+#pragma unroll
+        for (int i = 0; i < CH / 4; ++i) {
+          const int st = min(s0 + 4 * i + lg, nsteps - 1);
+          xsd[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, (int)xq_scale_off(units, mg * nsteps + st, lr), 0,
+                                                             kCoherent);
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          if (s0 + j < s_end) {
+            const int xs = __shfl(xsd[j >> 2], 16 * (j & 3) + lr) >> (8 * lg);
+#pragma unroll
+            for (int q = 0; q < NG; ++q) acc[q][mg] = mma(wf[q][j], xf[j], acc[q][mg], wscale(q, j), xs);
+          }
       }
     }
-
-  // 5. lane holds Y[16 mg + lr][n0 + 32 wave + 16 f + 4 lg .. + 3] of this slice
-  if (nslices == 1) {
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int mg = 0; mg < MG; ++mg) {
-        const int m = 16 * mg + lr;
-        if (m < g.m) store4(g, m, n0 + 32 * wave + 16 * f + 4 * lg, acc[f][mg], y_vec);
+  } else {
+    if ((int)blockIdx.x < nprod) produce<ROT, P, Q>(L, xr, units, nsteps, kblocks, nprod, lane);
+    if (lane == 0) {
+      const uint32_t* cnt = L.counters + CNT_PRODUCED + LLINE * (blockIdx.x % LREPL);
+      uint32_t polls = 0;
+      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)nprod) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++polls == LPOLL_LIMIT) {
+          __hip_atomic_store(L.counters + CNT_ERROR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
       }
+    }
+    __builtin_amdgcn_s_barrier();   // releases the compute waves
+    if (lane == 0) {
+      // this workgroup is past its poll: count it; the last one clears
+      const int grp = blockIdx.x / gsize;
+      const uint32_t members = (uint32_t)min(gsize, (int)gridDim.x - grp * gsize);
+      const uint32_t ngroups = (gridDim.x + gsize - 1) / gsize;
+      uint32_t* gc = L.counters + CNT_GROUP0 + LLINE * grp;
+      if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+        __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__hip_atomic_fetch_add(L.counters + CNT_TOP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            ngroups - 1) {
+          __hip_atomic_store(L.counters + CNT_TOP, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int r = 0; r < LREPL; ++r)
+            __hip_atomic_store(L.counters + CNT_PRODUCED + LLINE * r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+
+  // The compute waves' partial tiles summed in wave order, as
+  // gemm_small_kernel.  Wave 0 waits on an LDS count of the other compute
+  // waves, not at a workgroup barrier, which would also wait for the sync
+  // wave's counter round trips.
+  if (wave > 0) {
+    if (!compute) return;
+#pragma unroll
+    for (int q = 0; q < NG; ++q)
+#pragma unroll
+      for (int mg = 0; mg < MG; ++mg) red[wave][q * MG + mg][lane] = acc[q][mg];
+    if (lane == 0) __hip_atomic_fetch_add(&red_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     return;
   }
-  // Partial tiles go through device-coherent (sc1) stores, which write
-  // through this XCD's L2 to the memory side, and are read back with
-  // device-coherent loads: the same accesses as device-scope atomics, so no
-  // fence has to write back or invalidate whole caches (a release fence here,
-  // an L2 write-back per workgroup, cost more than the rest of the kernel).
-  // A wave's stores are complete once its store counter drains; the barrier
-  // then orders every wave's stores before the counter increment.
-  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(L.partials, 0, 0x7FFFFFFF, 0x00020000);
-  constexpr int kCoherent = 16;   // cache policy sc1: device scope
-  const int64_t slice_off = (int64_t)slice * g.m * L.ld_part;
+  if (nwaves > 1) {
+    // bounded: the other compute waves wait on nothing once their loads are
+    // in (the bound is far beyond any real wait)
+    for (uint32_t spins = 0;
+         __hip_atomic_load(&red_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)(nwaves - 1) &&
+         spins < (1u << 24);
+         ++spins)
+      __builtin_amdgcn_s_sleep(1);
+    for (int w2 = 1; w2 < nwaves; ++w2) {
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) acc[q][mg] += red[w2][q * MG + mg][lane];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NG; ++q)
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) {
       const int m = 16 * mg + lr;
-      if (m < g.m) {
-        const int64_t e = slice_off + (int64_t)m * L.ld_part + n0 + 32 * wave + 16 * f + 4 * lg;
-        const v4f a = acc[f][mg];
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]), __float_as_uint(a[3])}, prs,
-            (int)(e * 4), 0, kCoherent);
-      }
+      if (m < g.m) store4(g, m, n0 + 16 * q + 4 * lg, acc[q][mg], y_vec);
     }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(L.counters + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = done == (uint32_t)(nslices - 1);
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  // the last workgroup of the group: the S tiles summed in slice order
-  const int chunks = g.m * (LNR / 4);
-  for (int c = tid; c < chunks; c += 64 * LWAVES) {
-    const int m = c / (LNR / 4), col = n0 + 4 * (c % (LNR / 4));
-    const int64_t e = (int64_t)m * L.ld_part + col;
-    v4f v = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int sl = 0; sl < nslices; ++sl) {
-      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)((e + (int64_t)sl * g.m * L.ld_part) * 4), 0,
-                                                            kCoherent);
-      const v4f t = v4f{__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3])};
-      v = sl == 0 ? t : v + t;
-    }
-    store4(g, m, col, v, y_vec);
-  }
-  if (tid == 0) __hip_atomic_store(L.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// K split over the waves: chunks of CH steps, up to MAXW waves (the fused
+// layer takes the same split as the small-M GEMM, so their sums agree)
+void wave_split(int k, int& nwaves, int& spw) {
+  const int nsteps = (k + 127) / 128;
+  nwaves = (nsteps + CH - 1) / CH;
+  if (nwaves > MAXW) nwaves = MAXW;
+  if (nwaves < 1) nwaves = 1;
+  spw = (nsteps + nwaves - 1) / nwaves;
+}
+
+template <int MG, int NG, int WB, int ROT, int P, int Q>
+void launch_fused(const LinearArgs& L, int nwaves, int spw, int y_vec, hipStream_t s) {
+  const int grid = (L.g.n + 16 * NG - 1) / (16 * NG);
+  const int units = MG * ((L.g.k + 127) / 128);
+  const int nprod = min(min(units, grid), LPROD_MAX);
+  const int gsize = max(32, (grid + LGROUPS_MAX - 1) / LGROUPS_MAX);
+  const int threads = 64 * (nwaves + 1);
+  if (L.g.tiled)
+    linear_small_kernel<MG, NG, WB, ROT, P, Q, true><<<grid, threads, 0, s>>>(L, nwaves, spw, nprod, gsize, y_vec);
+  else
+    linear_small_kernel<MG, NG, WB, ROT, P, Q, false><<<grid, threads, 0, s>>>(L, nwaves, spw, nprod, gsize, y_vec);
+}
+
+// Up to 4 compute waves (k <= 4096): a register budget of two waves per
+// SIMD, which holds a chunk of 64 weight rows for one M group (32 rows for
+// more); past 4 compute waves, three waves per SIMD and half the rows.
 template <int MG, int ROT, int P, int Q>
-void launch_fused(const LinearArgs& L, int nslices, int y_vec, hipStream_t s) {
-  const dim3 grid((L.g.n + LNR - 1) / LNR, nslices);
-  if (L.g.tiled) linear_small_kernel<MG, ROT, P, Q, true><<<grid, 64 * LWAVES, 0, s>>>(L, nslices, y_vec);
-  else linear_small_kernel<MG, ROT, P, Q, false><<<grid, 64 * LWAVES, 0, s>>>(L, nslices, y_vec);
+void launch_fused_waves(const LinearArgs& L, int y_vec, hipStream_t s) {
+  int nwaves, spw;
+  wave_split(L.g.k, nwaves, spw);
+  if (nwaves <= 4) launch_fused<MG, MG == 1 ? 4 : 2, 5, ROT, P, Q>(L, nwaves, spw, y_vec, s);
+  else launch_fused<MG, MG <= 2 ? 2 : 1, MAXW + 1, ROT, P, Q>(L, nwaves, spw, y_vec, s);
 }
 
 template <int MG>
-hipError_t launch_fused_mg(const LinearArgs& L, int nslices, int y_vec, hipStream_t s) {
-  if (L.rot == 0) launch_fused<MG, 0, 1, 32>(L, nslices, y_vec, s);
-  else if (L.rot == 1) launch_fused<MG, 1, 1, 32>(L, nslices, y_vec, s);
-  else if (L.rot == 3) launch_fused<MG, 3, 1, 32>(L, nslices, y_vec, s);
+hipError_t launch_fused_mg(const LinearArgs& L, int y_vec, hipStream_t s) {
+  if (L.rot == 0) launch_fused_waves<MG, 0, 1, 32>(L, y_vec, s);
+  else if (L.rot == 1) launch_fused_waves<MG, 1, 1, 32>(L, y_vec, s);
+  else if (L.rot == 3) launch_fused_waves<MG, 3, 1, 32>(L, y_vec, s);
   else {
     switch (L.p) {
-      case 2: launch_fused<MG, 2, 2, 16>(L, nslices, y_vec, s); break;
-      case 4: launch_fused<MG, 2, 4, 8>(L, nslices, y_vec, s); break;
-      case 8: launch_fused<MG, 2, 8, 4>(L, nslices, y_vec, s); break;
-      case 16: launch_fused<MG, 2, 16, 2>(L, nslices, y_vec, s); break;
+      case 2: launch_fused_waves<MG, 2, 2, 16>(L, y_vec, s); break;
+      case 4: launch_fused_waves<MG, 2, 4, 8>(L, y_vec, s); break;
+      case 8: launch_fused_waves<MG, 2, 8, 4>(L, y_vec, s); break;
+      case 16: launch_fused_waves<MG, 2, 16, 2>(L, y_vec, s); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -662,11 +765,8 @@ bool linear_small_supported(const LinearArgs& L) {
 
 hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s) {
   if (!gemm_small_supported(g)) return hipErrorInvalidValue;
-  const int nsteps = (g.k + 127) / 128;
-  int nwaves = (nsteps + CH - 1) / CH;
-  if (nwaves > MAXW) nwaves = MAXW;
-  if (nwaves < 1) nwaves = 1;
-  const int spw = (nsteps + nwaves - 1) / nwaves;
+  int nwaves, spw;
+  wave_split(g.k, nwaves, spw);
   const size_t ybytes = g.y_bf16 ? 2 : 4;
   const int y_vec = (((uintptr_t)g.y) % (4 * ybytes) == 0) && (g.ld_y % 4 == 0);
   switch (g.m > 16 * MAXMG ? MAXMG : (g.m + 15) / 16) {
@@ -684,8 +784,8 @@ namespace mxfp4 {
 
 // ---------------------------------------------------------------------------
 // Fixed device scratch for mxfp4_linear_small_noalloc, the fused layer for
-// callers that cannot allocate: the workspace of the split over K lives in
-// this array, one copy per GPU, held until the process ends.  Host code never
+// callers that cannot allocate: the fused layer's workspace lives in this
+// array, one copy per GPU, held until the process ends.  Host code never
 // uses the array's name as an address: the device address comes from
 // hipGetSymbolAddress, once per device, with that device current.
 static __device__ __align__(256) uint8_t scratch[kLinearStaticScratchBytes];
@@ -720,32 +820,21 @@ hipError_t linear_small_static_scratch(void** ptr, hipStream_t s) {
   return hipSuccess;
 }
 
-int linear_small_slices(int64_t k) {
-  const int64_t nsteps = (k + 127) / 128;
-  return (int)((nsteps + LKS - 1) / LKS);
+int64_t linear_small_workspace_bytes(int64_t m, int64_t k) {
+  const int64_t units = (m + 15) / 16 * ((k + 127) / 128);
+  return kLinearCounterBytes + units * 1152;
 }
-
-int64_t linear_small_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  const int nslices = linear_small_slices(k);
-  if (nslices <= 1) return 0;
-  const int64_t groups = (n + LNR - 1) / LNR;
-  return linear_small_counter_bytes(n) + (int64_t)nslices * m * groups * LNR * 4;
-}
-
-int64_t linear_small_counter_bytes(int64_t) { return kLinearCounterBytes; }
 
 hipError_t launch_linear_small(const LinearArgs& L, hipStream_t s) {
-  if (!linear_small_supported(L)) return hipErrorInvalidValue;
-  const int nslices = linear_small_slices(L.g.k);
-  if (nslices > 1 && (L.counters == nullptr || L.partials == nullptr)) return hipErrorInvalidValue;
+  if (!linear_small_supported(L) || L.counters == nullptr || L.xq == nullptr) return hipErrorInvalidValue;
   const size_t ybytes = L.g.y_bf16 ? 2 : 4;
   const int y_vec = (((uintptr_t)L.g.y) % (4 * ybytes) == 0) && (L.g.ld_y % 4 == 0);
   hipError_t e;
   switch ((L.g.m + 15) / 16) {
-    case 1: e = launch_fused_mg<1>(L, nslices, y_vec, s); break;
-    case 2: e = launch_fused_mg<2>(L, nslices, y_vec, s); break;
-    case 3: e = launch_fused_mg<3>(L, nslices, y_vec, s); break;
-    default: e = launch_fused_mg<4>(L, nslices, y_vec, s); break;
+    case 1: e = launch_fused_mg<1>(L, y_vec, s); break;
+    case 2: e = launch_fused_mg<2>(L, y_vec, s); break;
+    case 3: e = launch_fused_mg<3>(L, y_vec, s); break;
+    default: e = launch_fused_mg<4>(L, y_vec, s); break;
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();

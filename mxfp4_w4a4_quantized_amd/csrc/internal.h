@@ -48,6 +48,10 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+int cu_count();
+
 // Large-tile persistent kernel (gemm_large.hip): K a multiple of 128,
 // 4-byte aligned scale pointers, operand code bytes below 4 GiB; the only
 // kernel for tiled operands.
@@ -62,9 +66,8 @@ bool gemm_small_supported(const GemmArgs& a);
 hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t s);
 
 // Fused small-M linear layer (gemm_small.hip): the activations are rotated
-// and quantized inside the GEMM, lane by lane, straight into the MFMA
-// operands (1 <= m <= 64; W in either layout, described by g.b_* / g.tiled;
-// g.a_* unused).
+// and quantized inside the GEMM kernel, in the same launch (1 <= m <= 64; W
+// in either layout, described by g.b_* / g.tiled; g.a_* unused).
 struct LinearArgs {
   const void* x;       // [m][ld_x] fp32 or bf16
   int64_t ld_x;        // elements
@@ -74,26 +77,22 @@ struct LinearArgs {
   const float* fa;
   const float* fb;
   GemmArgs g;
-  // split over K (more than one slice of 1024 elements): per-group counters
-  // (zero between calls) and fp32 partial tiles [slices][m][ld_part]
+  // workspace: handoff counters (zero between calls) and the quantized
+  // activations in MFMA operand order
   uint32_t* counters = nullptr;
-  float* partials = nullptr;
-  int64_t ld_part = 0;   // ceil(n / 256) * 256
+  uint8_t* xq = nullptr;
 };
 bool linear_small_supported(const LinearArgs& a);
 hipError_t launch_linear_small(const LinearArgs& a, hipStream_t s);
-// K slices of the fused layer, and the workspace it needs: a fixed region of
-// group counters (the same for every shape, so one workspace serves calls of
-// any shape) followed by the partial tiles; 0 for one slice.
-constexpr int64_t kLinearCounterBytes = 65536;             // 16384 groups of 256 weight rows
-constexpr int64_t kLinearMaxN = (kLinearCounterBytes / 4) * 256;
-int linear_small_slices(int64_t k);
+// Workspace of the fused layer: a fixed region of counters (the same for
+// every shape, so one workspace serves calls of any shape), then the
+// quantized activations, 1152 bytes per 16 rows and 128 K elements.
+constexpr int64_t kLinearCounterBytes = 4096;
+int64_t linear_small_workspace_bytes(int64_t m, int64_t k);
 // The fixed scratch of the allocation-free variant: its device address on
 // the current device (looked up, and its counters cleared on `s`, on the
 // first call per device).
-constexpr int64_t kLinearStaticScratchBytes = int64_t(16) << 20;
+constexpr int64_t kLinearStaticScratchBytes = int64_t(4) << 20;
 hipError_t linear_small_static_scratch(void** ptr, hipStream_t s);
-int64_t linear_small_counter_bytes(int64_t n);
-int64_t linear_small_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 }  // namespace mxfp4

@@ -42,7 +42,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mx.lib().mxfp4_abi_version() == 3
+    assert mx.lib().mxfp4_abi_version() == 4
     for s in range(4):
         assert mx.status_string(s).startswith("MXFP4_")
     assert "unknown" in mx.status_string(99)
@@ -160,39 +160,44 @@ def test_linear_small_argument_errors():
 
 
 def test_linear_small_workspace():
-    """Workspace size of the fused layer: none for one K slice (k <= 1024),
-    else 64 KiB of group counters plus the fp32 partial tiles; a missing or
-    short workspace is rejected synchronously."""
+    """Workspace size of the fused layer: 4 KiB of handoff counters plus 1152
+    bytes per 16 activation rows and 128 columns (the quantized activations
+    in operand order); a missing or short workspace is rejected
+    synchronously."""
     INV, UNS = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED
     A, T, BF, F = ALIGNED, mx.TILED, mx.MXFP4_BF16, mx.MXFP4_F32
     b = ctypes.c_int64()
     W = mx.lib().mxfp4_linear_small_workspace
-    assert mx.linear_small_workspace_bytes(16, 14336, 1024) == 0
-    groups = 14336 // 256
-    assert mx.linear_small_workspace_bytes(16, 14336, 4096) == 65536 + 4 * 16 * groups * 256 * 4
-    assert mx.linear_small_workspace_bytes(1, 300, 4128) == 65536 + 5 * 1 * 512 * 4
-    assert W(1, (1 << 22) + 1, 2048, ctypes.byref(b)) == UNS          # more than 16384 counters
+    assert mx.linear_small_workspace_bytes(16, 14336, 4096) == 4096 + 32 * 1152
+    assert mx.linear_small_workspace_bytes(16, 14336, 1024) == 4096 + 8 * 1152
+    assert mx.linear_small_workspace_bytes(1, 300, 4128) == 4096 + 33 * 1152      # ragged K: 33 steps
+    assert mx.linear_small_workspace_bytes(17, 300, 96) == 4096 + 2 * 1152        # two M groups, one step
+    assert mx.linear_small_workspace_bytes(64, 7, 4096) == 4096 + 4 * 32 * 1152
     assert mx.linear_small_workspace_bytes(0, 300, 4096) == 0
+    assert mx.linear_small_workspace_bytes(16, 0, 4096) == 0
     assert W(65, 300, 4096, ctypes.byref(b)) == UNS
-    assert W(64, 1 << 24, 8192, ctypes.byref(b)) == UNS              # partial tiles past 2 GiB
-    assert ls(A, BF, 64, 8192, 8192, None, A, A, 1 << 24, T, A, F, 1 << 24, A, 1 << 40, None) == UNS
+    assert W(64, 300, 1 << 29, ctypes.byref(b)) == UNS               # activation image past 2 GiB
+    assert ls(A, BF, 64, 1 << 29, 1 << 29, None, A, A, 8, T, A, F, 8, A, 1 << 40, None) == UNS
     assert W(4, 300, 48, ctypes.byref(b)) == INV
     assert W(4, 300, 64, None) == INV
     need = mx.linear_small_workspace_bytes(16, 512, 4096)
     assert ls(A, BF, 16, 4096, 4096, None, A, A, 512, T, A, F, 512, NULL, 0, None) == INV        # missing
     assert ls(A, BF, 16, 4096, 4096, None, A, A, 512, T, A, F, 512, A, need - 4, None) == INV    # short
     assert ls(A, BF, 16, 4096, 4096, None, A, A, 512, T, A, F, 512, A + 16, need, None) == UNS   # alignment
+    assert ls(A, BF, 16, 1024, 1024, None, A, A, 512, T, A, F, 512, NULL, 0, None) == INV        # any K needs one
 
 
 def test_linear_small_noalloc_rejects_before_any_device_work():
-    """The allocation-free fused layer checks its arguments and its 16 MiB
+    """The allocation-free fused layer checks its arguments and its 4 MiB
     scratch limit synchronously, before looking up or touching the scratch."""
     INV, UNS, OK = mx.MXFP4_ERR_INVALID_ARG, mx.MXFP4_ERR_UNSUPPORTED, mx.MXFP4_OK
     A, T, BF, F = ALIGNED, mx.TILED, mx.MXFP4_BF16, mx.MXFP4_F32
     na = mx.lib().mxfp4_linear_small_noalloc
-    assert mx.linear_small_workspace_bytes(16, 65536, 4096) > 16 << 20
-    assert na(A, BF, 16, 4096, 4096, None, A, A, 65536, T, A, F, 65536, None) == UNS     # past 16 MiB
-    assert na(A, BF, 64, 8192, 8192, None, A, A, 14336, T, A, F, 14336, None) == UNS     # past 16 MiB
+    assert mx.linear_small_workspace_bytes(16, 512, 465536) <= 4 << 20
+    assert mx.linear_small_workspace_bytes(16, 512, 465536 + 128) > 4 << 20
+    assert mx.linear_small_workspace_bytes(64, 512, 116352) <= 4 << 20
+    assert na(A, BF, 16, 465664, 465664, None, A, A, 512, T, A, F, 512, None) == UNS     # past 4 MiB
+    assert na(A, BF, 64, 116480, 116480, None, A, A, 512, T, A, F, 512, None) == UNS     # past 4 MiB
     assert na(A, BF, 65, 4096, 4096, None, A, A, 512, T, A, F, 512, None) == UNS         # m > 64
     assert na(A, BF, 16, 4096, 4096, None, NULL, A, 512, T, A, F, 512, None) == INV      # null weights
     assert na(NULL, BF, 0, 4096, 4096, None, NULL, NULL, 512, T, NULL, F, 512, None) == OK   # m == 0

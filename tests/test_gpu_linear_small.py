@@ -1,7 +1,7 @@
 """GPU parity of the fused small-M linear layer (mxfp4_linear_small): the
-activations are rotated and quantized inside the GEMM.
+activations are rotated and quantized inside the GEMM kernel.
 
-Two kinds of check:
+Three kinds of check:
   * Exact pin of the in-GEMM quantization.  With W the K x K identity
     (quantized without rotation: each row has one element 1.0, encoded exactly
     as code 4.0 at scale 2^-2), every output element is a single exact product,
@@ -11,6 +11,9 @@ Two kinds of check:
     activations, at the normalized 1e-5 bound of the GEMM tests, for random
     MXFP4 weights; bf16 output equal to the round-to-nearest-even bf16 of the
     same kernel's fp32 output.
+  * The layer against the unfused path (quantize_rotate, then gemm) on the
+    same inputs: bit-identical Y, since both take the same K split and
+    summation order.
 """
 import numpy as np
 import pytest
@@ -187,40 +190,88 @@ def test_fused_unsupported_cases_raise():
         mx.linear_small(x, wc, ws)                               # m > 64
 
 
+SAME_AS_SPLIT = [
+    (16, 14336, 4096, "tiled", (4, 8)), (1, 300, 4128, "rowmajor", None), (33, 70, 2048, "tiled", "h32"),
+    (64, 700, 12288, "tiled", "smooth"), (7, 77, 96, "rowmajor", (8, 4)), (24, 1000, 8192, "rowmajor", "h32"),
+    (48, 513, 1024, "tiled", (2, 16))]
+
+
+@pytest.mark.parametrize("m,n,k,layout,rot", SAME_AS_SPLIT, ids=str)
+def test_fused_equals_split_layer_bit_for_bit(m, n, k, layout, rot):
+    """The fused layer takes the small-M GEMM's K split and summation order,
+    so its Y equals quantize_rotate followed by gemm bit for bit (fp32 and
+    bf16), across M groups, the wave counts of long K (12288: 8 waves of 12
+    steps) and ragged K (4128)."""
+    rng = np.random.default_rng(3 * m + n + k)
+    x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
+    wc, ws = workloads.random_mxfp4(rng, n, k)
+    r = make_rot(rot, k=k)
+    lay = LAYOUTS[layout]
+    announce("linear_small vs split", m, n, k, layout, rot)
+    dwc, dws = weights_dev(wc, ws, lay)
+    xd = bf16_dev(x)
+    got = {}
+    for dt, bits in ((torch.float32, torch.int32), (torch.bfloat16, torch.int16)):
+        yf = mx.linear_small(xd, dwc, dws, r, dt, layout=lay, n=n)
+        ys = mx.linear(xd, dwc, dws, r, dt, layout=lay, n=n)
+        torch.cuda.synchronize()
+        assert torch.equal(yf.view(bits), ys.view(bits)), f"{dt}: fused and split outputs differ"
+        got[dt] = yf
+    xc, xs = oracle.quantize(x, rot=oracle_rot(r), bf16=True)
+    ref = oracle.gemm(xc, xs, wc, ws)
+    assert norm_err(got[torch.float32].cpu().numpy(), ref, row_norms(xc, xs), row_norms(wc, ws)) <= TOL
+
+
 @pytest.mark.parametrize("m,n,k,rot", [(16, 3000, 4096, (4, 8)), (64, 700, 12288, "h32"), (5, 256, 2048, None)],
                          ids=str)
-def test_split_k_workspace_contract(m, n, k, rot):
-    """Split over K (k > 1024): with a caller-supplied zeroed workspace, two
-    calls in a row give bit-identical Y (the partial tiles are summed in slice
-    order whichever workgroup finishes last), every group counter is back at
-    zero after each call, and Y meets the oracle bound."""
+def test_workspace_contract(m, n, k, rot):
+    """With a caller-supplied zeroed workspace, two calls in a row give
+    bit-identical Y, the handoff counters (the first 4 KiB, error word
+    included) are back at zero after each call, the workspace holds the
+    oracle's codes and scales in operand order, and Y meets the oracle
+    bound."""
     rng = np.random.default_rng(m + n + k)
     x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
     wc, ws = workloads.random_mxfp4(rng, n, k)
     r = make_rot(rot, k=k)
     need = mx.linear_small_workspace_bytes(m, n, k)
-    groups = -(-n // 256)
-    assert need > 65536
     work = torch.zeros(need, dtype=torch.uint8, device=DEV)
     dwc, dws = weights_dev(wc, ws, mx.TILED)
-    announce("linear_small split-k workspace", m, n, k, rot)
+    announce("linear_small workspace", m, n, k, rot)
     xd = bf16_dev(x)
     y1 = mx.linear_small(xd, dwc, dws, r, torch.float32, layout=mx.TILED, n=n, workspace=work)
     torch.cuda.synchronize()
-    assert not work[:4 * groups].any(), "group counters not reset"
+    assert not work[:4096].any(), "handoff counters not reset"
     y2 = mx.linear_small(xd, dwc, dws, r, torch.float32, layout=mx.TILED, n=n, workspace=work)
     torch.cuda.synchronize()
-    assert not work[:4 * groups].any(), "group counters not reset"
+    assert not work[:4096].any(), "handoff counters not reset"
     assert torch.equal(y1, y2)
     xc, xs = oracle.quantize(x, rot=oracle_rot(r), bf16=True)
+    # the activation image: unit (M group g, step s) = 64 lanes x 16 code
+    # bytes, lane l = block 4 s + l // 16 of row 16 g + l % 16; then per unit
+    # 16 dwords of the step's 4 scale bytes of each row, in 128-byte slots
+    img = work[4096:].cpu().numpy()
+    groups, nsteps = -(-m // 16), -(-k // 128)
+    units = groups * nsteps
+    codes = img[:units * 1024].reshape(groups, nsteps, 4, 16, 16)        # [g][s][block][row][16 B]
+    scales = img[units * 1024:units * 1152].reshape(groups, nsteps, 128)[:, :, :64].reshape(groups, nsteps, 16, 4)
+    pad_rows = groups * 16
+    xcp = np.zeros((pad_rows, nsteps * 64), np.uint8)
+    xsp = np.zeros((pad_rows, nsteps * 4), np.uint8)
+    xcp[:m, :k // 2] = xc
+    xsp[:m, :k // 32] = xs
+    want_c = xcp.reshape(groups, 16, nsteps, 4, 16).transpose(0, 2, 3, 1, 4)
+    want_s = xsp.reshape(groups, 16, nsteps, 4).transpose(0, 2, 1, 3)
+    assert np.array_equal(codes, want_c), "quantized activation codes in the workspace"
+    assert np.array_equal(scales, want_s), "quantized activation scales in the workspace"
     ref = oracle.gemm(xc, xs, wc, ws)
     assert norm_err(y1.cpu().numpy(), ref, row_norms(xc, xs), row_norms(wc, ws)) <= TOL
 
 
-def test_split_k_workspace_reused_across_shapes():
+def test_workspace_reused_across_shapes():
     """One workspace serves calls of different shapes in stream order: the
     counter region is the same for every shape and each call leaves it zero."""
-    shapes = [(16, 3000, 4096), (7, 9000, 2048), (33, 500, 8192), (16, 3000, 4096)]
+    shapes = [(16, 3000, 4096), (7, 9000, 2048), (33, 500, 8192), (64, 300, 512), (16, 3000, 4096)]
     need = max(mx.linear_small_workspace_bytes(m, n, k) for m, n, k in shapes)
     work = torch.zeros(need, dtype=torch.uint8, device=DEV)
     for i, (m, n, k) in enumerate(shapes):
@@ -231,7 +282,7 @@ def test_split_k_workspace_reused_across_shapes():
         dwc, dws = weights_dev(wc, ws, mx.TILED)
         y = mx.linear_small(bf16_dev(x), dwc, dws, "h32", torch.float32, layout=mx.TILED, n=n, workspace=work)
         torch.cuda.synchronize()
-        assert not work[:65536].any(), "counters not reset"
+        assert not work[:4096].any(), "counters not reset"
         xc, xs = oracle.quantize(x, rot="h32", bf16=True)
         ref = oracle.gemm(xc, xs, wc, ws)
         assert norm_err(y.cpu().numpy(), ref, row_norms(xc, xs), row_norms(wc, ws)) <= TOL
