@@ -63,10 +63,12 @@ __device__ __forceinline__ void kron32(const float* __restrict__ fa, const float
                                        float (&v)[32]) {
   static_assert(P * Q == 32, "P*Q must be 32");
   float u[32];
+  // row k of B is used by all P chains of stage 1 at once (fewer factor
+  // registers live at a time than going block row by block row)
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
+  for (int k = 0; k < Q; ++k) {
 #pragma unroll
-    for (int k = 0; k < Q; ++k) {
+    for (int j = 0; j < P; ++j) {
       float acc = fb[k * Q] * v[Q * j];
 #pragma unroll
       for (int l = 1; l < Q; ++l) acc = __builtin_fmaf(fb[k * Q + l], v[Q * j + l], acc);
