@@ -395,8 +395,10 @@ void launch_mg(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s)
 //  * The compute waves issue their first chunk of weight loads before that
 //    barrier, so the weight stream (the layer's HBM-bound part) runs while X
 //    is quantized and handed over.  After the barrier they read the
-//    quantized X with device-coherent loads, which cannot hit a stale L2 copy
-//    from an earlier call, and run the MFMAs as the weights arrive.
+//    quantized X with device-scope coherent loads (the coherence the compiler
+//    gives agent-scope atomic loads, so no copy of a line from an earlier
+//    call is returned; the fetch counters show these reads served inside the
+//    XCDs' L2) and run the MFMAs as the weights arrive.
 // The compute waves never poll themselves.  A wave's vector loads complete
 // in order, so a poll issued behind a weight chunk would wait for all of it.
 // A workgroup that waits holds its CU, and a workgroup of 5 or 9 waves takes
