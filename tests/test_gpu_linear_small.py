@@ -288,3 +288,56 @@ def test_workspace_reused_across_shapes():
         xc, xs = oracle.quantize(x, rot="h32", bf16=True)
         ref = oracle.gemm(xc, xs, wc, ws)
         assert norm_err(y.cpu().numpy(), ref, row_norms(xc, xs), row_norms(wc, ws)) <= TOL
+
+
+@pytest.mark.parametrize("rot", ["h32", (4, 8)], ids=str)
+def test_back_to_back_calls_see_their_own_activations(rot):
+    """Calls in a row on one workspace, with different activations and no
+    synchronization between them, each read the activations they quantized,
+    not a copy left in some L2 by the call before: every Y equals the unfused
+    path's bit for bit.  Then the same through a captured graph of three
+    calls, replayed three times with new activations copied in between."""
+    m, n, k = 16, 3000, 4096
+    rng = np.random.default_rng(77)
+    wc, ws = workloads.random_mxfp4(rng, n, k)
+    dwc, dws = weights_dev(wc, ws, mx.TILED)
+    r = make_rot(rot, k=k)
+
+    def fresh_x():
+        return bf16_dev(workloads.bf16_bits(workloads.random_blocks(rng, m, k)))
+
+    def split(x):
+        return mx.linear(x, dwc, dws, r, torch.float32, layout=mx.TILED, n=n)
+
+    work = torch.zeros(mx.linear_small_workspace_bytes(m, n, k), dtype=torch.uint8, device=DEV)
+    xs = [fresh_x() for _ in range(8)]
+    ys = [torch.empty(m, n, dtype=torch.float32, device=DEV) for _ in xs]
+    announce("linear_small back to back", m, n, k, rot)
+    for x, y in zip(xs, ys):
+        mx.linear_small(x, dwc, dws, r, torch.float32, y=y, layout=mx.TILED, n=n, workspace=work)
+    torch.cuda.synchronize()
+    for i, (x, y) in enumerate(zip(xs, ys)):
+        assert torch.equal(y, split(x)), f"call {i} of a back-to-back run"
+
+    announce("linear_small graph replays", m, n, k, rot)
+    xg = [fresh_x() for _ in range(3)]
+    yg = [torch.empty(m, n, dtype=torch.float32, device=DEV) for _ in xg]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        for x, y in zip(xg, yg):
+            mx.linear_small(x, dwc, dws, r, torch.float32, y=y, layout=mx.TILED, n=n, workspace=work)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for x, y in zip(xg, yg):
+            mx.linear_small(x, dwc, dws, r, torch.float32, y=y, layout=mx.TILED, n=n, workspace=work)
+    for rep in range(3):
+        for x in xg:
+            x.copy_(fresh_x())
+        graph.replay()
+        torch.cuda.synchronize()
+        assert not work[:4096].any(), "handoff counters not reset"
+        for i, (x, y) in enumerate(zip(xg, yg)):
+            assert torch.equal(y, split(x)), f"replay {rep}, call {i}"

@@ -42,3 +42,26 @@ def test_noalloc_matches_workspace_entry_point_on_two_calls():
         ref = oracle.gemm(xc, xs, wc, ws)
         den = np.outer(np.sqrt((oracle.dequantize(xc, xs) ** 2).sum(1)), np.sqrt((oracle.dequantize(wc, ws) ** 2).sum(1)))
         assert (np.abs(y_na.cpu().numpy().astype(np.float64) - ref) <= TOL * den).all(), f"call {i}: oracle bound"
+
+
+def test_noalloc_back_to_back_calls():
+    """Calls in a row on the fixed scratch, with different activations and no
+    synchronization between them, each read the activations they quantized:
+    every Y equals the workspace entry point's on the same input."""
+    m, n, k = 16, 3000, 4096
+    rng = np.random.default_rng(91)
+    wc, ws = workloads.random_mxfp4(rng, n, k)
+    tc, ts = mx.tile_host(wc, ws)
+    dwc = torch.from_numpy(tc).to(DEV)
+    dws = torch.from_numpy(ts).to(DEV)
+    xs = [torch.from_numpy(workloads.bf16_bits(workloads.random_blocks(rng, m, k)).view(np.int16)).to(DEV)
+          .view(torch.bfloat16) for _ in range(8)]
+    print(f"[case] linear_small_noalloc back to back: m={m} n={n} k={k}", flush=True)
+    ys = [torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV) for _ in xs]
+    for x, y in zip(xs, ys):
+        mx.linear_small_noalloc(x, dwc, dws, y, "h32", layout=mx.TILED)
+    torch.cuda.synchronize()
+    work = torch.zeros(mx.linear_small_workspace_bytes(m, n, k), dtype=torch.uint8, device=DEV)
+    for i, (x, y) in enumerate(zip(xs, ys)):
+        y_ws = mx.linear_small(x, dwc, dws, "h32", torch.float32, layout=mx.TILED, n=n, workspace=work)
+        assert torch.equal(y, y_ws), f"call {i} of a back-to-back run"
