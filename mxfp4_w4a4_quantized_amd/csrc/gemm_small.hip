@@ -483,6 +483,19 @@ __device__ __forceinline__ void produce(const LinearArgs& L, const __amdgpu_buff
                                         int kblocks, int nprod, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const uint8_t* xb = static_cast<const uint8_t*>(L.x);
+  // Kronecker factors (4 x 8 and 8 x 4: 80 values) are read before the first
+  // block and ahead of the compute waves' weight stream.  Read where the
+  // chains first use them, these uniform loads were issued after the block
+  // had arrived and then waited microseconds behind the weight loads.
+  constexpr bool FPRE = ROT == 2 && P * P + Q * Q <= 80;
+  float fa_r[FPRE ? P * P : 1], fb_r[FPRE ? Q * Q : 1];
+  if constexpr (FPRE) {
+#pragma unroll
+    for (int i = 0; i < P * P; ++i) fa_r[i] = L.fa[i];
+#pragma unroll
+    for (int i = 0; i < Q * Q; ++i) fb_r[i] = L.fb[i];
+  }
+  __builtin_amdgcn_sched_barrier(0);
   for (int u = blockIdx.x; u < units; u += nprod) {
     const int mg = u / nsteps, s = u - mg * nsteps;
     const int row = 16 * mg + lr, c = 4 * s + lg;
@@ -491,7 +504,8 @@ __device__ __forceinline__ void produce(const LinearArgs& L, const __amdgpu_buff
     load_block<true>(xb + ((int64_t)(ok ? row : 0) * L.ld_x + (int64_t)(ok ? c : 0) * 32) * 2, ok, raw);
     u32x4 codes;
     int sb;
-    quantize_raw<true, ROT, P, Q>(raw, ROT == 3 ? L.fa + 32 * min(c, kblocks - 1) : L.fa, L.fb, codes, sb);
+    quantize_raw<true, ROT, P, Q>(raw, ROT == 3 ? L.fa + 32 * min(c, kblocks - 1) : (FPRE ? fa_r : L.fa),
+                                  FPRE ? fb_r : L.fb, codes, sb);
     if (!ok) {   // rows past M and blocks past K: zero codes, zero scale byte
       codes = u32x4{0u, 0u, 0u, 0u};
       sb = 0;
@@ -595,6 +609,11 @@ __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int
   // path (no register of one path is live on the other).  A bare barrier: a
   // workgroup fence would wait for the weight loads in flight.
   if (compute) {
+    // The weight stream starts about 0.4 us after the producers' first loads.
+    // Issued at once, it filled the memory queues ahead of those loads, and
+    // the producers' blocks, factors and store acknowledgements waited
+    // behind it (handoff at 7 us instead of 3).
+    __builtin_amdgcn_s_sleep(16);
     if (s_begin < s_end) load_weights(s_begin);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");   // keeps the activation loads below the barrier
