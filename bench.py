@@ -22,9 +22,10 @@ Prints one JSON line:
               it (`split` or `fused`)
   roofline    the dominant kernel (the GEMM, or the fused layer for decode
               shapes, bytes = bf16 X + MXFP4 W + Y), its launch time the mean
-              over K launches of that kernel alone, back to back over the
-              buffer sets and replayed from HIP graphs of at least 64
-              launches, with HIP events on the launch stream around the loop.  `us_marked` gives the mean, median and min of a loop of
+              over at least max(K, 200) launches of that kernel alone (`launches`), back
+              to back over the buffer sets, as whole replays of a HIP graph of
+              at least 64 launches after untimed ones, with HIP events on the
+              launch stream around the loop.  `us_marked` gives the mean, median and min of a loop of
               the K steps with events around every launch (each marker adds a
               dispatch gap, which inflates short kernels).  Large M: the
               MFMA-bound large-tile kernel, algorithmic FLOPs per launch / its
@@ -283,6 +284,8 @@ def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0):
         tail = capture(parts, rest) if rest else None
         for _ in range(max(1, warmup // per)):
             cycle.replay()
+        if tail is not None:   # a graph's first replay is slower: not in the timed loop
+            tail.replay()
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -300,17 +303,39 @@ def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0):
     if use_fused:
         graph_ms["fused"] = time_graph(fused)
 
-    # Per-launch duration of one kernel: `steps` launches of it alone, back to
-    # back over the buffer sets, replayed from graphs of at least 64 launches
-    # (so that the host's graph-launch cost stays hidden behind the GPU work
-    # even for a few-microsecond kernel), with HIP events on the launch stream
+    # Per-launch duration of one kernel: launches of it alone, back to back
+    # over the buffer sets, as whole replays of one graph of at least 64
+    # launches (so that the host's graph-launch cost stays hidden behind the
+    # GPU work even for a few-microsecond kernel), at least max(steps, 200)
+    # launches in all, after untimed replays; HIP events on the launch stream
     # around the whole loop and none between launches: the kernel's duration
     # plus the dispatch gap between two launches, without the gap each event
-    # marker adds (which dominates short kernels).
+    # marker adds (which dominates short kernels).  A kernel property, so its
+    # window does not shrink with --steps: at --steps 20, exactly 20 launches
+    # (one replay of a fresh 20-launch graph) read 81 us per flux_up GEMM,
+    # and one replay of 80 launches 79.6-80.8 us, against 76.7 us over 240
+    # (the first launches after a change of kernel run slower).
     alone_per_replay = nsets * -(-64 // nsets)
+    alone_reps = max(1, -(-max(steps, 200) // alone_per_replay))
+    alone_launches = alone_reps * alone_per_replay
+
+    def time_alone_ms(parts):
+        cycle = capture(parts, alone_per_replay)
+        for _ in range(max(1, warmup // alone_per_replay)):
+            cycle.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(alone_reps):
+            cycle.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        del cycle
+        return t0.elapsed_time(t1) / alone_launches
 
     def time_alone(f):
-        return time_graph([f], alone_per_replay) / steps
+        return time_alone_ms([f])
 
     q_alone, g_alone = time_alone(split[0]), time_alone(split[1])
     if use_fused:
@@ -377,7 +402,7 @@ def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0):
             if st != 0:
                 raise RuntimeError(f"mxfp4_ceiling_stream failed: HIP error {st}")
         saved, sets[:] = list(sets), bufs
-        ms = time_graph([launch], alone_per_replay) / steps
+        ms = time_alone_ms([launch])
         sets[:] = saved
         moved = waves * (rk + wk) * 1024
         read_ceiling[cname] = {"us_per_launch": ms * 1e3, "bytes": moved, "gbps": moved / (ms * 1e-3) / 1e9}
@@ -462,7 +487,7 @@ def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0):
     return dict(ceiling=ceiling, m=m, n=n, k=k, wl=wl, total_ms=total_ms, wall_s=wall, q_ms=q_ms, g_ms=g_ms,
                 q_alone=q_alone, g_alone=g_alone, graph_ms=graph_ms, read_ceiling=read_ceiling, outputs=outputs,
                 power=power, fused=fused_res, copy_gbps=copy_gbps, transforms=transforms, wfit=wfit,
-                requant=requant_ms, nsets=nsets, device=props.name,
+                requant=requant_ms, nsets=nsets, alone_launches=alone_launches, device=props.name,
                 cus=props.multi_processor_count, arch=getattr(props, "gcnArchName", ""))
 
 
@@ -772,8 +797,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_MXFP4_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_MXFP4_TFLOPS, 4), "kernel": gkernel}
-    roof.update({"traffic": traffic, "us_per_launch": round(g_us, 2), "us_marked": marked(g["g_ms"]),
-                 "algorithmic_bytes": g_bytes, "algorithmic_flops": flops})
+    roof.update({"traffic": traffic, "us_per_launch": round(g_us, 2), "launches": g["alone_launches"],
+                 "us_marked": marked(g["g_ms"]), "algorithmic_bytes": g_bytes, "algorithmic_flops": flops})
     split_info = {"ms_per_step": per_path["quantize+gemm"], "quantize_us": round(q_us, 2), "gemm_us": round(g_us, 2)}
     fz = g["fused"]
     if best_path != "fused":
@@ -794,7 +819,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(f_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(f_gbps / PEAK_HBM_GBPS, 4), "frac_of_copy": round(f_gbps / g["copy_gbps"], 4),
                 "kernel": "linear_small", "traffic": f_traffic,
-                "us_per_launch": round(f_us, 2), "us_marked": marked(fz["ms"]),
+                "us_per_launch": round(f_us, 2), "launches": g["alone_launches"], "us_marked": marked(fz["ms"]),
                 "algorithmic_bytes": f_bytes, "algorithmic_flops": flops}
     metric = METRIC if args.workload == "flux_up" else \
         f"MXFP4 GEMM TFLOPS @ M={m},K={k},N={n} (% peak); quantize GB/s (% HBM)"
@@ -822,7 +847,8 @@ def main():
                      "frac_of_copy": round(q_gbps / g["copy_gbps"], 4),
                      "frac_of_read_ceiling": (round(rc_["quantize"]["us_per_launch"] / q_us, 4)
                                               if "quantize" in rc_ else None),
-                     "traffic": q_traffic, "us_per_launch": round(q_us, 2), "us_marked": marked(g["q_ms"]),
+                     "traffic": q_traffic, "us_per_launch": round(q_us, 2), "launches": g["alone_launches"],
+                     "us_marked": marked(g["q_ms"]),
                      "algorithmic_bytes": q_bytes},
         "split": split_info if fz is not None else None,
         "fused": fused_only,
