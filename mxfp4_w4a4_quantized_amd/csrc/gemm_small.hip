@@ -612,7 +612,7 @@ __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int
     // The weight stream starts about 0.4 us after the producers' first loads.
     // Issued at once, it filled the memory queues ahead of those loads, and
     // the producers' blocks, factors and store acknowledgements waited
-    // behind it (handoff at 7 us instead of 3).
+    // behind it (a producer's block arrived after 4.8 us instead of 1.9).
     __builtin_amdgcn_s_sleep(16);
     if (s_begin < s_end) load_weights(s_begin);
     __builtin_amdgcn_s_barrier();
