@@ -96,10 +96,12 @@ def test_random_operands(m, n, k):
 # see FEW_TILE_SHAPES): one K stage, fewer stages than the load ring, ragged
 # M and N, fewer tiles than CUs (grid not a multiple of 8), and more tiles
 # than CUs (several tiles per workgroup, the load ring running across tile
-# boundaries).
+# boundaries; 289, 432 and 560 tiles run as 2, 2 and 3 full rounds on 152,
+# 216 and 192 workgroups).
 LARGE_SHAPES = [
     (2304, 512, 128), (1030, 2100, 256), (520, 1030, 384), (96, 2048, 512),
     (2200, 100, 640), (1024, 768, 1024), (4352, 4352, 128), (2304, 4608, 384),
+    (3000, 9000, 128), (5000, 7000, 256),
 ]
 
 
