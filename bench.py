@@ -11,7 +11,10 @@ codes, scales, Y) that the working set exceeds the 256 MB Infinity Cache.
 
 Prints one JSON line:
   value       2*M*N*K / (time of one step), TFLOP/s, from HIP events around
-              the whole loop of K steps (no event markers between launches).
+              the whole loop of K steps (no event markers between launches),
+              after --settle-ms of untimed steps and the W warm-up steps (the
+              engine clock dips for the first ~17 ms of load after an idle
+              gap; settle_ms in the line).
               A step is one quantize + GEMM.  For decode shapes (M <= 64,
               bf16 activations) both that and one launch of the fused layer
               (mxfp4_linear_small) are timed.  Each path is timed launched
@@ -92,6 +95,7 @@ METRIC = "MXFP4 GEMM TFLOPS @ M=3584,K=3072,N=12288 (% peak); quantize GB/s (% H
 PEAK_MXFP4_TFLOPS = 10100.0     # MI355X dense FP4/FP6 MFMA
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 CACHE_BUST_BYTES = 600 << 20    # working set per cycle of buffer sets (> 256 MB)
+SETTLE_S = 0.05                 # untimed runs of the work before each timed loop (--settle-ms)
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mxfp4_w4a4_quantized_amd", "csrc")
 
@@ -162,7 +166,7 @@ def _sse(codes, scales, ref):
 
 # ----------------------------------------------------------------- GPU leg ---
 
-def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0):
+def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0, settle_s: float = SETTLE_S):
     import torch
     import mxfp4_w4a4_quantized_amd as mx
 
@@ -211,6 +215,24 @@ def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0):
 
     stream = torch.cuda.current_stream(dev)   # the stream every launch goes to
 
+    def settle(run_once):
+        """Untimed runs of the work about to be timed, for settle_s seconds,
+        right before its warm-up steps: after an idle gap (the host's set-up,
+        a graph capture) the engine clock first overshoots downwards, and the
+        first ~17 ms of flux_up steps ran ~10% slower than the rest (88-90 vs
+        79 us per step in 200-step windows after 1 s idle, then flat for the
+        next 0.6 s).  The timed loop then measures the rate the load settles
+        to, as a serving loop sees it."""
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        n = 0
+        while n < 2 or time.perf_counter() - t_start < settle_s:
+            run_once()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()   # the host stays a few launches ahead, no more
+        torch.cuda.synchronize()
+
     def time_loop(parts, marks):
         """Time `steps` steps with HIP events on the launch stream around the
         whole loop; with `marks`, also around every part of every step.  An
@@ -219,6 +241,14 @@ def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0):
         launch's start with the previous one's end: the step time comes from a
         loop without them, the per-launch durations from a second loop with
         them."""
+        cyc = [0]
+
+        def one_step():
+            s_ = sets[cyc[0] % nsets]
+            cyc[0] += 1
+            for f in parts:
+                f(s_)
+        settle(one_step)
         for i in range(warmup):
             for f in parts:
                 f(sets[i % nsets])
@@ -282,6 +312,7 @@ def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0):
         cycle = capture(parts, per)
         rest = steps % per
         tail = capture(parts, rest) if rest else None
+        settle(cycle.replay)
         for _ in range(max(1, warmup // per)):
             cycle.replay()
         if tail is not None:   # a graph's first replay is slower: not in the timed loop
@@ -321,6 +352,7 @@ def gpu_leg(name: str, steps: int, warmup: int, power_seconds: float = 0.0):
 
     def time_alone_ms(parts):
         cycle = capture(parts, alone_per_replay)
+        settle(cycle.replay)
         for _ in range(max(1, warmup // alone_per_replay)):
             cycle.replay()
         torch.cuda.synchronize()
@@ -742,16 +774,19 @@ def main():
                     help="rows of X in the oracle's CPU sample (-1: all rows, at most 8192; 0 skips the CPU leg)")
     ap.add_argument("--power-seconds", type=float, default=3.0,
                     help="seconds of back-to-back launches per phase of the clock and power trace (0 skips it)")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_S * 1e3,
+                    help="untimed runs of the timed work before its warm-up steps, in ms, so that the timed "
+                         "loop runs at the clock the load settles to (0: only the warm-up steps)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    if args.steps < 1 or args.warmup < 0:
-        ap.error("--steps must be >= 1 and --warmup >= 0")
+    if args.steps < 1 or args.warmup < 0 or args.settle_ms < 0:
+        ap.error("--steps must be >= 1, --warmup >= 0 and --settle-ms >= 0")
 
-    g = gpu_leg(args.workload, args.steps, args.warmup, args.power_seconds)
+    g = gpu_leg(args.workload, args.steps, args.warmup, args.power_seconds, args.settle_ms * 1e-3)
     m, n, k, wl = g["m"], g["n"], g["k"], g["wl"]
     flops = 2.0 * m * n * k
     # the step: the fastest of the two-launch path and the fused layer, each
@@ -834,6 +869,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
