@@ -112,6 +112,16 @@ __device__ __forceinline__ float acc_read(float x) {
   return r;
 }
 
+// A zero accumulator, written by one v_accvgpr_write whose result the
+// compiler cannot see as a constant.  With a plain 0.f the compiler
+// materialized the 256 zeros of a tile twice (once for a K loop that might
+// not run), 512 register writes per tile instead of 256.
+__device__ __forceinline__ float acc_zero() {
+  float r;
+  asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(r));
+  return r;
+}
+
 __device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = GROUP_M * tiles_n;
   const int grp = L / per_group;
@@ -307,7 +317,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
 #pragma unroll
       for (int c = 0; c < FM; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[a][c][r] = acc_zero();
 
     for (int kt = 0; kt < nk; ++kt) {
       advance();   // to stage it + NBUF - 1 (its branch stays out of the MFMA block)
