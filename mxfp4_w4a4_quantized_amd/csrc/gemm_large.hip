@@ -112,14 +112,24 @@ __device__ __forceinline__ float acc_read(float x) {
   return r;
 }
 
-// A zero accumulator, written by one v_accvgpr_write whose result the
-// compiler cannot see as a constant.  With a plain 0.f the compiler
+// Zero accumulators at the start of a tile.  With a plain 0.f the compiler
 // materialized the 256 zeros of a tile twice (once for a K loop that might
-// not run), 512 register writes per tile instead of 256.
+// not run), 512 register writes per wave and tile.  An opaque zero cannot be
+// rematerialized: acc_zero() is one v_accvgpr_write (the fp32-output kernel),
+// acc_zero_mfma() one MFMA of zero codes with a zero accumulator input that
+// clears a whole fragment's 16 registers on the matrix pipe, which is idle
+// between tiles (the bf16 and MXFP4-output kernels, whose epilogues read every
+// accumulator through acc_read).  Both compiled without spills; zeros from
+// the MFMA builtin, or a first K stage started from the MFMA's zero operand,
+// made the compiler copy or spill the accumulators.
 __device__ __forceinline__ float acc_zero() {
   float r;
   asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(r));
   return r;
+}
+
+__device__ __forceinline__ void acc_zero_mfma(v16f& acc, const u32x4& zero_codes) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %1, 0 cbsz:4 blgp:4" : "=a"(acc) : "v"(zero_codes));
 }
 
 __device__ __forceinline__ void tile_coords(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -310,14 +320,30 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
 
   constexpr int NRD = FN + FM;                  // fragment reads per sub-step
   int cbuf = 0;   // ring slot of the stage being computed
+  u32x4 zero_codes;
+  {
+    uint32_t z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    zero_codes = u32x4{z, z, z, z};
+  }
   for (int j = 0; j * nk < total; ++j) {
     v16f acc[FN][FM];
+    if constexpr (OUT == 0) {
 #pragma unroll
-    for (int a = 0; a < FN; ++a)
+      for (int a = 0; a < FN; ++a)
 #pragma unroll
-      for (int c = 0; c < FM; ++c)
+        for (int c = 0; c < FM; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][c][r] = acc_zero();
+          for (int r = 0; r < 16; ++r) acc[a][c][r] = acc_zero();
+    } else {
+#pragma unroll
+      for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int c = 0; c < FM; ++c) acc_zero_mfma(acc[a][c], zero_codes);
+      // the compiler does not see these MFMAs: wait states before a later
+      // MFMA takes their results as its accumulator input
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    }
 
     for (int kt = 0; kt < nk; ++kt) {
       advance();   // to stage it + NBUF - 1 (its branch stays out of the MFMA block)
@@ -504,8 +530,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int n = tn * BN + wn * (BN / WN) + 32 * a + 8 * t + 4 * lg;
-          const float v0 = acc[a][bb][4 * t], v1 = acc[a][bb][4 * t + 1];
-          const float v2 = acc[a][bb][4 * t + 2], v3 = acc[a][bb][4 * t + 3];
+          float v0, v1, v2, v3;
+          if constexpr (BF16OUT) {   // every bf16 read goes through acc_read (above)
+            v0 = acc_read(acc[a][bb][4 * t]), v1 = acc_read(acc[a][bb][4 * t + 1]);
+            v2 = acc_read(acc[a][bb][4 * t + 2]), v3 = acc_read(acc[a][bb][4 * t + 3]);
+          } else {
+            v0 = acc[a][bb][4 * t], v1 = acc[a][bb][4 * t + 1];
+            v2 = acc[a][bb][4 * t + 2], v3 = acc[a][bb][4 * t + 3];
+          }
           if constexpr (BF16OUT) {
             uint16_t* yp = static_cast<uint16_t*>(g.y) + (int64_t)m * g.ld_y + n;
             const uint32_t lo = pack_bf16(v0, v1), hi = pack_bf16(v2, v3);
