@@ -377,16 +377,25 @@ void launch_mg(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s)
 // The compute waves are those of gemm_small_kernel: K split over the waves
 // in chunks of CH steps (the same split), the same MFMA chains and the same
 // LDS reduction, so Y equals mxfp4_quantize_rotate followed by mxfp4_gemm
-// bit for bit.  A workgroup takes 16 NG weight rows and has one more wave,
-// its sync wave:
-//  * The sync waves of the first `nprod` workgroups rotate and quantize X.
-//    A pass takes one unit of 16 rows x 128 elements (one K step of one M
-//    group), one block per lane, with the quantizer's own arithmetic
-//    (block_quant.h).  The codes and scales go into the workspace already in
-//    MFMA operand order, through device-coherent (sc1) stores that write
-//    through the XCD's L2.  The wave waits for its stores, then counts its
-//    workgroup on a device-scope counter, kept in 16 copies on separate
-//    lines.
+// bit for bit.  A compute workgroup takes 16 NG weight rows and has one more
+// wave, its sync wave.
+//  * Producers rotate and quantize X.  A pass takes one unit of 16 rows x 128
+//    elements (one K step of one M group), one block per lane, with the
+//    quantizer's own arithmetic (block_quant.h).  The codes and scales go
+//    into the workspace already in MFMA operand order, through
+//    device-coherent (sc1) stores that write through the XCD's L2.  A
+//    producer wave waits for its stores, then counts itself on a
+//    device-scope counter, kept in 16 copies on separate lines.
+//  * Where the compute grid leaves CUs idle and they have a wave for every
+//    unit (the decode shapes: 224 workgroups on 256 CUs), the producers are
+//    `pwg` extra workgroups ahead of the compute ones, one per idle CU.  A
+//    CU's vector memory requests are served in order, so a producer sharing
+//    its CU with four compute waves waited behind their weight loads: its
+//    block, its store acknowledgements and its count each took microseconds
+//    longer.  On a CU of their own the layer took 9.1 instead of 10.4 us at
+//    16 x 4096 -> 14336.  Otherwise the sync waves of the first `nprod`
+//    compute workgroups produce, and the compute waves hold back their
+//    weight stream for about 0.4 us so that the producers' loads go first.
 //  * Every sync wave polls one copy of that counter until all producers have
 //    counted, then releases its workgroup's compute waves at a barrier.
 //    (With one copy, the increments queued behind a couple of hundred
@@ -410,7 +419,7 @@ void launch_mg(const GemmArgs& g, int nwaves, int spw, int y_vec, hipStream_t s)
 // second round.
 //
 // Termination.  Producers wait on nothing before they count, and they are
-// the lowest-numbered workgroups, which the dispatcher places first.  The
+// in the lowest-numbered workgroups, which the dispatcher places first.  The
 // poll is bounded all the same (2^20 polls, tens of milliseconds); past the
 // bound the sync wave sets an error word in the workspace and goes on, and
 // that call's Y is undefined.
@@ -476,11 +485,11 @@ __device__ __forceinline__ uint32_t xq_scale_off(int units, int u, int row) {
   return (uint32_t)units * 1024u + (uint32_t)u * 128u + 4u * row;
 }
 
-// Sync wave of a producer workgroup: quantize its units of X into the
-// workspace, then count the workgroup once its stores have completed.
+// A producer wave: quantize units first, first + stride, ... of X into the
+// workspace, then count itself once its stores have completed.
 template <int ROT, int P, int Q>
 __device__ __forceinline__ void produce(const LinearArgs& L, const __amdgpu_buffer_rsrc_t& xr, int units, int nsteps,
-                                        int kblocks, int nprod, int lane) {
+                                        int kblocks, int first, int stride, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const uint8_t* xb = static_cast<const uint8_t*>(L.x);
   // Kronecker factors (4 x 8 and 8 x 4: 80 values) are read before the first
@@ -496,7 +505,7 @@ __device__ __forceinline__ void produce(const LinearArgs& L, const __amdgpu_buff
     for (int i = 0; i < Q * Q; ++i) fb_r[i] = L.fb[i];
   }
   __builtin_amdgcn_sched_barrier(0);
-  for (int u = blockIdx.x; u < units; u += nprod) {
+  for (int u = first; u < units; u += stride) {
     const int mg = u / nsteps, s = u - mg * nsteps;
     const int row = 16 * mg + lr, c = 4 * s + lg;
     const bool ok = row < L.g.m && c < kblocks;
@@ -527,7 +536,7 @@ __device__ __forceinline__ void produce(const LinearArgs& L, const __amdgpu_buff
 // WB: waves per workgroup the kernel is compiled for (compute waves + 1).
 template <int MG, int NG, int WB, int ROT, int P, int Q, bool TILED>
 __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int nwaves, int spw, int nprod,
-                                                                 int gsize, int y_vec) {
+                                                                 int ncount, int pwg, int gsize, int y_vec) {
   static_assert(MG * NG <= 2 * MAXACC, "reduction buffer size");
   static_assert(CH % 4 == 0, "dword scale loads cover 4 steps");
   __shared__ v4f red[MAXW][MG * NG][64];
@@ -537,7 +546,7 @@ __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16 * NG;
+  const int cb = (int)blockIdx.x - pwg;   // compute workgroup index
   const int kblocks = g.k >> 5;
   const int nsteps = (g.k + 127) >> 7;
   const int units = MG * nsteps;
@@ -549,6 +558,14 @@ __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int
   const int s_begin = wave * spw;
   const int s_end = min(nsteps, s_begin + spw);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(L.xq, 0, units * 1152, 0x00020000);
+  if (cb < 0) {
+    // producer workgroup, on a CU with no weight stream: each wave with
+    // units quantizes them and counts itself
+    const int first = wave * pwg + (int)blockIdx.x;
+    if (first < units) produce<ROT, P, Q>(L, xr, units, nsteps, kblocks, first, pwg * (nwaves + 1), lane);
+    return;
+  }
+  const int n0 = cb * 16 * NG;
 
   Operand w[NG];
 #pragma unroll
@@ -609,11 +626,13 @@ __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int
   // path (no register of one path is live on the other).  A bare barrier: a
   // workgroup fence would wait for the weight loads in flight.
   if (compute) {
-    // The weight stream starts about 0.4 us after the producers' first loads.
-    // Issued at once, it filled the memory queues ahead of those loads, and
-    // the producers' blocks, factors and store acknowledgements waited
-    // behind it (a producer's block arrived after 4.8 us instead of 1.9).
-    __builtin_amdgcn_s_sleep(16);
+    // With producers in the compute workgroups, the weight stream starts
+    // about 0.4 us after their first loads.  Issued at once, it filled the
+    // memory queues ahead of those loads, and the producers' blocks, factors
+    // and store acknowledgements waited behind it (a producer's block arrived
+    // after 4.8 us instead of 1.9).  Producers on CUs of their own need no
+    // delay (with it: 9.5 instead of 9.1 us).
+    if (pwg == 0) __builtin_amdgcn_s_sleep(16);
     if (s_begin < s_end) load_weights(s_begin);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");   // keeps the activation loads below the barrier
@@ -659,11 +678,11 @@ __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int
       }
     }
   } else {
-    if ((int)blockIdx.x < nprod) produce<ROT, P, Q>(L, xr, units, nsteps, kblocks, nprod, lane);
+    if (cb < nprod) produce<ROT, P, Q>(L, xr, units, nsteps, kblocks, cb, nprod, lane);
     if (lane == 0) {
-      const uint32_t* cnt = L.counters + CNT_PRODUCED + LLINE * (blockIdx.x % LREPL);
+      const uint32_t* cnt = L.counters + CNT_PRODUCED + LLINE * (cb % LREPL);
       uint32_t polls = 0;
-      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)nprod) {
+      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)ncount) {
         __builtin_amdgcn_s_sleep(1);
         if (++polls == LPOLL_LIMIT) {
           __hip_atomic_store(L.counters + CNT_ERROR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -674,9 +693,10 @@ __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int
     __builtin_amdgcn_s_barrier();   // releases the compute waves
     if (lane == 0) {
       // this workgroup is past its poll: count it; the last one clears
-      const int grp = blockIdx.x / gsize;
-      const uint32_t members = (uint32_t)min(gsize, (int)gridDim.x - grp * gsize);
-      const uint32_t ngroups = (gridDim.x + gsize - 1) / gsize;
+      const int ncomp = (int)gridDim.x - pwg;
+      const int grp = cb / gsize;
+      const uint32_t members = (uint32_t)min(gsize, ncomp - grp * gsize);
+      const uint32_t ngroups = (ncomp + gsize - 1) / gsize;
       uint32_t* gc = L.counters + CNT_GROUP0 + LLINE * grp;
       if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
         __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -742,13 +762,20 @@ template <int MG, int NG, int WB, int ROT, int P, int Q>
 void launch_fused(const LinearArgs& L, int nwaves, int spw, int y_vec, hipStream_t s) {
   const int grid = (L.g.n + 16 * NG - 1) / (16 * NG);
   const int units = MG * ((L.g.k + 127) / 128);
-  const int nprod = min(min(units, grid), LPROD_MAX);
+  // producer workgroups on the CUs the compute grid leaves idle, if they
+  // have a wave for every unit; else producers in the compute workgroups
+  const int idle = cu_count() - grid;
+  const int pwg = idle > 0 && idle * (nwaves + 1) >= units ? min(idle, units) : 0;
+  const int nprod = pwg ? 0 : min(min(units, grid), LPROD_MAX);
+  const int ncount = pwg ? min(units, pwg * (nwaves + 1)) : nprod;
   const int gsize = max(32, (grid + LGROUPS_MAX - 1) / LGROUPS_MAX);
   const int threads = 64 * (nwaves + 1);
   if (L.g.tiled)
-    linear_small_kernel<MG, NG, WB, ROT, P, Q, true><<<grid, threads, 0, s>>>(L, nwaves, spw, nprod, gsize, y_vec);
+    linear_small_kernel<MG, NG, WB, ROT, P, Q, true><<<grid + pwg, threads, 0, s>>>(L, nwaves, spw, nprod, ncount, pwg,
+                                                                                    gsize, y_vec);
   else
-    linear_small_kernel<MG, NG, WB, ROT, P, Q, false><<<grid, threads, 0, s>>>(L, nwaves, spw, nprod, gsize, y_vec);
+    linear_small_kernel<MG, NG, WB, ROT, P, Q, false><<<grid + pwg, threads, 0, s>>>(L, nwaves, spw, nprod, ncount, pwg,
+                                                                                     gsize, y_vec);
 }
 
 // Up to 4 compute waves (k <= 4096): a register budget of two waves per
