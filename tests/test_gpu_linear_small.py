@@ -194,7 +194,11 @@ SAME_AS_SPLIT = [
     (16, 14336, 4096, "tiled", (4, 8)), (1, 300, 4128, "rowmajor", None), (33, 70, 2048, "tiled", "h32"),
     (64, 700, 12288, "tiled", "smooth"), (7, 77, 96, "rowmajor", (8, 4)), (24, 1000, 8192, "rowmajor", "h32"),
     (48, 513, 1024, "tiled", (2, 16)), (16, 4096, 14336, "tiled", (4, 8)), (30, 333, 8320, "rowmajor", (2, 16)),
-    (5, 256, 16384, "tiled", (16, 2))]
+    (5, 256, 16384, "tiled", (16, 2)),
+    # on 256 CUs: 250 compute workgroups leave too few idle CUs for the 32
+    # units (producers in the compute workgroups); 240 leave 16 (producer
+    # workgroups with two producing waves each); 200 with 3-wave workgroups
+    (16, 16000, 4096, "tiled", (4, 8)), (16, 15360, 4096, "tiled", "h32"), (9, 12800, 2048, "rowmajor", None)]
 
 
 @pytest.mark.parametrize("m,n,k,layout,rot", SAME_AS_SPLIT, ids=str)
@@ -202,8 +206,9 @@ def test_fused_equals_split_layer_bit_for_bit(m, n, k, layout, rot):
     """The fused layer takes the small-M GEMM's K split and summation order,
     so its Y equals quantize_rotate followed by gemm bit for bit (fp32 and
     bf16), across M groups, the wave counts of long K (12288: 8 waves of 12
-    steps; 14336 and 16384 with Kronecker transforms), ragged K (4128, 8320)
-    and both weight layouts."""
+    steps; 14336 and 16384 with Kronecker transforms), ragged K (4128, 8320),
+    both weight layouts, and both producer placements (workgroups of their own
+    on idle CUs, or the compute workgroups' sync waves)."""
     rng = np.random.default_rng(3 * m + n + k)
     x = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
     wc, ws = workloads.random_mxfp4(rng, n, k)
