@@ -347,17 +347,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
         for (int c = 0; c < FM; ++c)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[a][c][r] = acc_zero();
-    } else {
-      if constexpr (OUT == 1) {
+    } else if constexpr (OUT == 1) {
 #pragma unroll
-        for (int a = 0; a < FN; ++a)
+      for (int a = 0; a < FN; ++a)
 #pragma unroll
-          for (int c = 0; c < FM; ++c) acc_zero_mfma(acc[a][c], zero_codes);
-      }
-      // the compiler does not see these MFMAs: wait states before a later
-      // MFMA takes their results as its accumulator input
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        for (int c = 0; c < FM; ++c) acc_zero_mfma(acc[a][c], zero_codes);
     }
+    // the compiler does not see these clears (inline asm): wait states before
+    // the K loop's MFMAs take them as their accumulator input
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     for (int kt = 0; kt < nk; ++kt) {
       advance();   // to stage it + NBUF - 1 (its branch stays out of the MFMA block)
