@@ -328,12 +328,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
     zero_codes = u32x4{z, z, z, z};
   }
-  // MXFP4 output: each fragment is cleared in the epilogue right after its
-  // accumulators are read, so the clearing MFMAs overlap the epilogue's other
-  // work (bit-identical, 1% faster at 3584 x 3072 -> 12288 and 57344 x 3072 ->
-  // 21504); the other kernels clear at the top of each tile
+  // bf16 and MXFP4 output: each fragment is cleared in the epilogue right
+  // after its accumulators are read, so the clearing MFMAs overlap the
+  // epilogue's other work (bit-identical, 1-2% faster than clearing at the
+  // top of each tile); the fp32-output kernel writes its zeros at the top
   v16f acc[FN][FM];
-  if constexpr (OUT == 2) {
+  if constexpr (OUT != 0) {
 #pragma unroll
     for (int a = 0; a < FN; ++a)
 #pragma unroll
@@ -347,11 +347,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
         for (int c = 0; c < FM; ++c)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[a][c][r] = acc_zero();
-    } else if constexpr (OUT == 1) {
-#pragma unroll
-      for (int a = 0; a < FN; ++a)
-#pragma unroll
-        for (int c = 0; c < FM; ++c) acc_zero_mfma(acc[a][c], zero_codes);
     }
     // the compiler does not see these clears (inline asm): wait states before
     // the K loop's MFMAs take them as their accumulator input
@@ -477,13 +472,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
       continue;
     }
     if constexpr (WN == 2 && WM == 2) {
-      // Interior tiles: stage each wave's 128 x 128 output block through the
-      // ring slot of the stage just computed (free until the next issue,
-      // which follows the next barrier), 32 rows x 256 bytes at a time in a
-      // padded 32 x 272-byte area (4 bf16 or 2 fp32 fragments per pass), then
-      // store 4 full 256-byte rows per instruction (16 bytes per lane) instead
-      // of short pieces of 32 rows.
-      if (y_st && (tm + 1) * BM <= g.m && (tn + 1) * BN <= g.n) {
+      // Stage each wave's 128 x 128 output block through the ring slot of
+      // the stage just computed (free until the next issue, which follows the
+      // next barrier), 32 rows x 256 bytes at a time in a padded 32 x
+      // 272-byte area (4 bf16 or 2 fp32 fragments per pass), then store 4
+      // full 256-byte rows per instruction (16 bytes per lane) instead of
+      // short pieces of 32 rows.  Edge tiles and output rows that do not
+      // start 16-byte aligned take the same staging with bounds-checked
+      // stores, so there is one epilogue path: with two, the compiler copied
+      // the accumulators to move their clearing into the epilogue.  bf16:
+      // each fragment is cleared right after it is read.
+      {
+        const bool full = y_st && (tm + 1) * BM <= g.m && (tn + 1) * BN <= g.n;
         constexpr int PITCH = 272;
         constexpr int ESZ = BF16OUT ? 2 : 4;
         constexpr int FPP = 256 / (32 * ESZ);   // fragments per pass
@@ -502,6 +502,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
               if constexpr (BF16OUT) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) v[r] = acc_read(acc[a][bb][r]);
+                acc_zero_mfma(acc[a][bb], zero_codes);
               }
 #pragma unroll
               for (int t = 0; t < 4; ++t) {
@@ -518,22 +519,48 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
             // the area is private to this wave: its LDS writes land before its reads
             const int m0 = tm * BM + wm * (BM / WM) + 32 * bb;
             const int64_t n0 = tn * BN + wn * (BN / WN) + a0 * 32 + (lane & 15) * (16 / ESZ);
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              const int row = 4 * r + (lane >> 4);
-              const uint4 v = *reinterpret_cast<const uint4*>(tb + row * PITCH + (lane & 15) * 16);
-              // non-temporal: Y streams out without displacing the operand
-              // panels the XCD's other workgroups still read from L2
-              __builtin_nontemporal_store(
-                  u32x4{v.x, v.y, v.z, v.w},
-                  reinterpret_cast<u32x4*>(static_cast<uint8_t*>(g.y) + ((int64_t)(m0 + row) * g.ld_y + n0) * ESZ));
+              for (int r = 0; r < 8; ++r) {
+                const int row = 4 * r + (lane >> 4);
+                const uint4 v = *reinterpret_cast<const uint4*>(tb + row * PITCH + (lane & 15) * 16);
+                // non-temporal: Y streams out without displacing the operand
+                // panels the XCD's other workgroups still read from L2
+                __builtin_nontemporal_store(
+                    u32x4{v.x, v.y, v.z, v.w},
+                    reinterpret_cast<u32x4*>(static_cast<uint8_t*>(g.y) + ((int64_t)(m0 + row) * g.ld_y + n0) * ESZ));
+              }
+            } else {
+              // edge tiles and unaligned rows: bounds-checked stores of the same staged rows
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                const int row = 4 * r + (lane >> 4);
+                const uint4 v = *reinterpret_cast<const uint4*>(tb + row * PITCH + (lane & 15) * 16);
+                if (m0 + row < g.m) {
+                  uint8_t* yp = static_cast<uint8_t*>(g.y) + ((int64_t)(m0 + row) * g.ld_y + n0) * ESZ;
+                  if (y_st && n0 + 16 / ESZ <= g.n) {
+                    *reinterpret_cast<uint4*>(yp) = v;
+                  } else {
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 16 / ESZ; ++e) {
+                      if (n0 + e < g.n) {
+                        if constexpr (ESZ == 2)
+                          reinterpret_cast<uint16_t*>(yp)[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                        else
+                          reinterpret_cast<uint32_t*>(yp)[e] = w4[e];
+                      }
+                    }
+                  }
+                }
+              }
             }
           }
         }
         continue;
       }
     }
-    if constexpr (OUT != 2) {
+    if constexpr (OUT != 2 && !(WN == 2 && WM == 2)) {
 #pragma unroll
     for (int bb = 0; bb < FM; ++bb) {
       const int m = tm * BM + wm * (BM / WM) + 32 * bb + lr;
