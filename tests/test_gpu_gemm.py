@@ -130,23 +130,36 @@ def test_few_tile_shapes(m, n, k):
         test_tiled_operands(m, n, k)
 
 
-def test_large_tile_strided_output():
+@pytest.mark.parametrize("dt,off", [(torch.float32, 4), (torch.float32, 1), (torch.bfloat16, 4), (torch.bfloat16, 8)],
+                         ids=["f32-aligned", "f32-unaligned", "bf16-unaligned", "bf16-aligned"])
+def test_large_tile_strided_output(dt, off):
+    """Y inside a wider buffer (ld_y = n + 12) at an element offset, on a shape
+    with edge tiles in both dimensions: rows that start 16-byte aligned (the
+    staged epilogue's 16-byte stores, bounds-checked at the edges) and rows
+    that do not (element stores).  fp32 Y is checked against the oracle; bf16
+    Y must equal the kernel's own fp32 Y (contiguous) rounded to nearest even,
+    bit for bit; nothing outside Y may be written."""
     rng = np.random.default_rng(80)
     m, n, k = 520, 2100, 256
     ac, as_ = workloads.random_mxfp4(rng, m, k)
     bc, bs = workloads.random_mxfp4(rng, n, k)
-    for dt, fill in ((torch.float32, 7.0), (torch.bfloat16, 3.0)):
-        big = torch.full((m, n + 12), fill, dtype=dt, device=DEV)
-        y = big[:, 4:4 + n]                                          # ld_y = n + 12, offset 4
-        announce("gemm large strided", m, n, k, dt)
-        mx.gemm(*map(to_dev, (ac, as_, bc, bs)), dt, y=y)
-        torch.cuda.synchronize()
+    fill = 7.0 if dt == torch.float32 else 3.0
+    big = torch.full((m, n + 12), fill, dtype=dt, device=DEV)
+    y = big[:, off:off + n]
+    announce("gemm large strided", m, n, k, dt, off)
+    ops = list(map(to_dev, (ac, as_, bc, bs)))
+    mx.gemm(*ops, dt, y=y)
+    y32 = mx.gemm(*ops, torch.float32)
+    torch.cuda.synchronize()
+    if dt == torch.float32:
         ref = oracle.gemm(ac, as_, bc, bs)
-        if dt == torch.float32:
-            err = norm_err(y.cpu().numpy(), ref, row_norms(ac, as_), row_norms(bc, bs))
-            assert err <= TOL
-        host = big.float().cpu().numpy()
-        assert (host[:, :4] == fill).all() and (host[:, 4 + n:] == fill).all()   # no stray writes
+        assert norm_err(y.cpu().numpy(), ref, row_norms(ac, as_), row_norms(bc, bs)) <= TOL
+        assert torch.equal(y, y32), "strided fp32 Y differs from the contiguous one"
+    else:
+        assert torch.equal(y.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16)), \
+            "bf16 Y is not the round-to-nearest-even of the kernel's fp32 Y"
+    host = big.float().cpu().numpy()
+    assert (host[:, :off] == fill).all() and (host[:, off + n:] == fill).all()   # no stray writes
 
 
 TILED_SHAPES = [
