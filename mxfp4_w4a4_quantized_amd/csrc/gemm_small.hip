@@ -293,20 +293,64 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
     }
   }
 
+  // lane holds Y[m0 + 16 mg + lr][n .. n + 3] of weight group q
+  auto store_frag = [&](int q, int mg, const v4f& v) {
+    const int n = n0 + 16 * q + 4 * lg;
+    const int m = m0 + 16 * mg + lr;
+    if (m >= g.m) return;
+    if constexpr (BF16OUT) {
+      uint16_t* yp = static_cast<uint16_t*>(g.y) + (int64_t)m * g.ld_y + n;
+      if (y_vec && n + 3 < g.n) {
+        *reinterpret_cast<uint2*>(yp) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < g.n) yp[r] = (uint16_t)(pack_bf16(v[r], 0.f) & 0xFFFFu);
+      }
+    } else {
+      float* yp = static_cast<float*>(g.y) + (int64_t)m * g.ld_y + n;
+      if (y_vec && n + 3 < g.n) {
+        *reinterpret_cast<float4*>(yp) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < g.n) yp[r] = v[r];
+      }
+    }
+  };
+
+  // The waves' partial tiles are summed in wave order (wave 0's, then wave
+  // 1's, ...).  MXFP4 output: wave 0 sums and requantizes the 32-row block.
+  // Otherwise each fragment is summed and stored by one wave, so the sums and
+  // stores of the tile's fragments run on several waves at once.
   if (nwaves > 1) {
-    if (wave > 0) {
+    if constexpr (OUT == 2) {
+      if (wave > 0) {
+#pragma unroll
+        for (int q = 0; q < NG; ++q)
+#pragma unroll
+          for (int mg = 0; mg < MG; ++mg) red[wave][q * MG + mg][lane] = acc[q][mg];
+      }
+      __syncthreads();
+      if (wave > 0) return;
+      for (int w2 = 1; w2 < nwaves; ++w2) {
+#pragma unroll
+        for (int q = 0; q < NG; ++q)
+#pragma unroll
+          for (int mg = 0; mg < MG; ++mg) acc[q][mg] += red[w2][q * MG + mg][lane];
+      }
+    } else {
 #pragma unroll
       for (int q = 0; q < NG; ++q)
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) red[wave][q * MG + mg][lane] = acc[q][mg];
-    }
-    __syncthreads();
-    if (wave > 0) return;
-    for (int w2 = 1; w2 < nwaves; ++w2) {
-#pragma unroll
-      for (int q = 0; q < NG; ++q)
-#pragma unroll
-        for (int mg = 0; mg < MG; ++mg) acc[q][mg] += red[w2][q * MG + mg][lane];
+      __syncthreads();
+      for (int f = wave; f < MG * NG; f += nwaves) {
+        v4f sum = red[0][f][lane];
+        for (int w2 = 1; w2 < nwaves; ++w2) sum += red[w2][f][lane];
+        store_frag(f / MG, f % MG, sum);
+      }
+      return;
     }
   }
 
@@ -314,36 +358,12 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_small_kernel(GemmArgs g, int s
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) store_requant(g, m0 + 16 * mg + lr, n0, acc[0][mg], acc[NG - 1][mg], lane);
     return;
+  } else {
+#pragma unroll
+    for (int q = 0; q < NG; ++q)
+#pragma unroll
+      for (int mg = 0; mg < MG; ++mg) store_frag(q, mg, acc[q][mg]);
   }
-  // lane holds Y[m0 + 16 mg + lr][n .. n + 3] of weight group q
-#pragma unroll
-  for (int q = 0; q < NG; ++q)
-#pragma unroll
-    for (int mg = 0; mg < MG; ++mg) {
-      const int n = n0 + 16 * q + 4 * lg;
-      const int m = m0 + 16 * mg + lr;
-      if (m >= g.m) continue;
-      const v4f v = acc[q][mg];
-      if constexpr (BF16OUT) {
-        uint16_t* yp = static_cast<uint16_t*>(g.y) + (int64_t)m * g.ld_y + n;
-        if (y_vec && n + 3 < g.n) {
-          *reinterpret_cast<uint2*>(yp) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < g.n) yp[r] = (uint16_t)(pack_bf16(v[r], 0.f) & 0xFFFFu);
-        }
-      } else {
-        float* yp = static_cast<float*>(g.y) + (int64_t)m * g.ld_y + n;
-        if (y_vec && n + 3 < g.n) {
-          *reinterpret_cast<float4*>(yp) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < g.n) yp[r] = v[r];
-        }
-      }
-    }
 }
 
 template <int MG, int NG, int OUT, bool TILED>
@@ -732,41 +752,41 @@ __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int
     }
   }
 
-  // The compute waves' partial tiles summed in wave order, as
-  // gemm_small_kernel.  Wave 0 waits on an LDS count of the other compute
-  // waves, not at a workgroup barrier, which would also wait for the sync
-  // wave's counter round trips.
-  if (wave > 0) {
-    if (!compute) return;
+  // The compute waves' partial tiles summed in wave order (wave 0's, then
+  // wave 1's, ...), as gemm_small_kernel does, but each fragment summed and
+  // stored by one wave: every compute wave parks its partial tile in LDS and
+  // counts itself, waits for the count of all compute waves (an LDS count, not
+  // a workgroup barrier, which would also wait for the sync wave's counter
+  // round trips), then sums and stores fragments wave, wave + nwaves, ...
+  if (!compute) return;
+  if (nwaves == 1) {
 #pragma unroll
     for (int q = 0; q < NG; ++q)
 #pragma unroll
-      for (int mg = 0; mg < MG; ++mg) red[wave][q * MG + mg][lane] = acc[q][mg];
-    if (lane == 0) __hip_atomic_fetch_add(&red_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (int mg = 0; mg < MG; ++mg) {
+        const int m = 16 * mg + lr;
+        if (m < g.m) store4(g, m, n0 + 16 * q + 4 * lg, acc[q][mg], y_vec);
+      }
     return;
-  }
-  if (nwaves > 1) {
-    // bounded: the other compute waves wait on nothing once their loads are
-    // in (the bound is far beyond any real wait)
-    for (uint32_t spins = 0;
-         __hip_atomic_load(&red_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)(nwaves - 1) &&
-         spins < (1u << 24);
-         ++spins)
-      __builtin_amdgcn_s_sleep(1);
-    for (int w2 = 1; w2 < nwaves; ++w2) {
-#pragma unroll
-      for (int q = 0; q < NG; ++q)
-#pragma unroll
-        for (int mg = 0; mg < MG; ++mg) acc[q][mg] += red[w2][q * MG + mg][lane];
-    }
   }
 #pragma unroll
   for (int q = 0; q < NG; ++q)
 #pragma unroll
-    for (int mg = 0; mg < MG; ++mg) {
-      const int m = 16 * mg + lr;
-      if (m < g.m) store4(g, m, n0 + 16 * q + 4 * lg, acc[q][mg], y_vec);
-    }
+    for (int mg = 0; mg < MG; ++mg) red[wave][q * MG + mg][lane] = acc[q][mg];
+  if (lane == 0) __hip_atomic_fetch_add(&red_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // bounded: the compute waves wait on nothing once their loads are in (the
+  // bound is far beyond any real wait)
+  for (uint32_t spins = 0;
+       __hip_atomic_load(&red_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)nwaves &&
+       spins < (1u << 24);
+       ++spins)
+    __builtin_amdgcn_s_sleep(1);
+  for (int f = wave; f < MG * NG; f += nwaves) {
+    v4f sum = red[0][f][lane];
+    for (int w2 = 1; w2 < nwaves; ++w2) sum += red[w2][f][lane];
+    const int m = 16 * (f % MG) + lr;
+    if (m < g.m) store4(g, m, n0 + 16 * (f / MG) + 4 * lg, sum, y_vec);
+  }
 }
 
 // K split over the waves: chunks of CH steps, up to MAXW waves (the fused
