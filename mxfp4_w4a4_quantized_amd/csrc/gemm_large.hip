@@ -347,6 +347,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_large_kernel(GemmArgs g, int tiles
         for (int c = 0; c < FM; ++c)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[a][c][r] = acc_zero();
+    } else if constexpr (OUT == 1 && !(WN == 2 && WM == 2)) {
+      // other wave layouts (MXFP4_GEMM_WN / _WM) take the direct-store
+      // epilogue, which does not clear: clear here
+#pragma unroll
+      for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int c = 0; c < FM; ++c) acc_zero_mfma(acc[a][c], zero_codes);
     }
     // the compiler does not see these clears (inline asm): wait states before
     // the K loop's MFMAs take them as their accumulator input
