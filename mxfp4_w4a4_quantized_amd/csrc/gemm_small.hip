@@ -670,12 +670,12 @@ __global__ __launch_bounds__(64 * WB) void linear_small_kernel(LinearArgs L, int
     for (int s0 = s_begin; s0 < s_end; s0 += CH) {
       if (s0 != s_begin) load_weights(s0);
       s0c = s0;
-      // One M group: the weight scales spread now, as the small-M GEMM does
-      // right after its weight loads (this waits for the chunk; the
-      // activation loads follow): 11.2 instead of 11.6 us at 16 x 4096 ->
-      // 14336.  More M groups: spread at each MFMA, so that the first group's
-      // activation loads go out before the weights are in (18.8 instead of
-      // 21.8 us at 64 rows).
+      // One M group: the weight scales spread now, before the activation
+      // loads (from LDS with tiled weights; dword loads, which wait for the
+      // chunk, with row-major ones: 11.2 instead of 11.6 us at 16 x 4096 ->
+      // 14336 when those were the tiled path too).  More M groups: spread at
+      // each MFMA, so that the first group's activation loads go out before
+      // the weights are in (18.8 instead of 21.8 us at 64 rows).
       int wsv[NG][CH];
       if constexpr (MG == 1) {
 #pragma unroll
