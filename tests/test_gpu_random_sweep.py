@@ -19,8 +19,10 @@ Checks, the same bars as the fixed-shape tests:
     tests); bf16 output the round-to-nearest-even bf16 of the same kernel's
     fp32 output.
 
-Two more draws use the same bars: the fused small-M layer (quantization
-inside the GEMM; bf16 activations, M <= 64, Kronecker 2 <= p <= 16), and the
+Three more draws use the same bars: the fused small-M layer (quantization
+inside the GEMM; bf16 activations, M <= 64, Kronecker 2 <= p <= 16), the same
+on wide weights (8000..24000 rows, K up to 8192; there the fused fp32 Y must
+also equal the split path's bit for bit), and the
 GEMM with an MXFP4 output on operands whose block exponents lie in [-1, 1],
 where Y is exact in fp32 and the requantized bytes must equal the oracle
 quantizer's on the oracle's Y.
@@ -150,6 +152,52 @@ def test_random_fused_small_m_case(i):
     y32 = mx.linear_small(xd, *wd, dev_rot, torch.float32, layout=layout, n=n)
     y = mx.linear_small(xd, *wd, dev_rot, out, layout=layout, n=n)
     torch.cuda.synchronize()
+    xc, xs = oracle.quantize(xh, rot=ref_rot, bf16=True)
+    ref = oracle.gemm(xc, xs, wc, ws)
+    den = np.outer(row_norms(xc, xs), row_norms(wc, ws))
+    diff = np.abs(y32.cpu().numpy().astype(np.float64) - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(den > 0, diff / den, np.where(diff == 0, 0.0, np.inf))
+    err = float(rel.max()) if rel.size else 0.0
+    assert err <= TOL, f"normalized error {err:.3e}"
+    if out == torch.bfloat16:
+        assert torch.equal(y.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+
+
+WIDE_CASES = 6
+
+
+@pytest.mark.parametrize("i", range(WIDE_CASES))
+def test_random_fused_wide_case(i):
+    """The fused layer on 8000..24000 weight rows and K up to 8192: grids of
+    about a hundred to several hundred workgroups (past the CU count the
+    producers sit in the compute workgroups), and up to 8 compute waves.  Its
+    fp32 Y must equal the split path's (quantizer, then GEMM) bit for bit and
+    be within the bound of the oracle."""
+    rng = np.random.default_rng(50000 + i)
+    m = int(rng.integers(1, 65))
+    n = int(rng.integers(8000, 24000))
+    tiled = rng.random() < 0.6
+    k = 32 * int(rng.integers(1, 257))
+    if tiled:
+        k = 128 * max(1, k // 128)
+    rot = FUSED_ROTS[int(rng.integers(0, 4))]
+    pq = KRON_PQ[int(rng.integers(0, len(KRON_PQ)))]
+    out = torch.float32 if rng.random() < 0.5 else torch.bfloat16
+    layout = mx.TILED if tiled else mx.ROWMAJOR
+    print(f"[case] fused wide {i}: m={m} n={n} k={k} tiled={tiled} rot={rot}"
+          f"{pq if rot == 'kron' else ''} out={out}", flush=True)
+    xh = workloads.bf16_bits(workloads.random_blocks(rng, m, k))
+    dev_rot, ref_rot = make_rot(rot, pq, k, rng)
+    wc, ws = workloads.random_mxfp4(rng, n, k)
+    wd = [to_dev(t) for t in (mx.tile_host(wc, ws) if tiled else (wc, ws))]
+    xd = to_dev(xh.view(np.int16)).view(torch.bfloat16)
+    y32 = mx.linear_small(xd, *wd, dev_rot, torch.float32, layout=layout, n=n)
+    y = mx.linear_small(xd, *wd, dev_rot, out, layout=layout, n=n)
+    ac, as_ = mx.quantize_rotate(xd, dev_rot, layout=layout)
+    ys = mx.gemm(ac, as_, *wd, torch.float32, layout=layout, m=m, n=n)
+    torch.cuda.synchronize()
+    assert torch.equal(ys.view(torch.int32), y32.view(torch.int32)), "fused and split fp32 Y differ"
     xc, xs = oracle.quantize(xh, rot=ref_rot, bf16=True)
     ref = oracle.gemm(xc, xs, wc, ws)
     den = np.outer(row_norms(xc, xs), row_norms(wc, ws))
